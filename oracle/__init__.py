@@ -1,0 +1,257 @@
+"""CPU oracle for the absmax-scaled quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``precision_quantized_gemm_amd``) and neither
+imports the other; the product path never falls back to it.
+
+The arithmetic lives in ``qlinear_oracle.c`` (plain C, double precision where
+the pages leave the precision open).  This module only builds that file with
+gcc, loads it with ctypes and marshals numpy arrays.  Each wrapper names the
+passage its C function follows; see the C file's header for the sources:
+
+* AstrAI ``astrai/extension/ops/fp8.py`` @ 5e76fbd (module docstring,
+  ``_fp8_quantize_cpu``, ``fp8_gemm``/``mm_fp8``/``linear_forward_fp8``
+  docstrings),
+* POPCORNBENCH "Kimi-K2.6 l2_p13" trace (reference-model steps 2-4 and the
+  round-half-to-even discussion),
+* scmp_kernels README ("API": per_tensor / per_row, ``a @ b.T``).
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+(codec enumeration, hand-worked fixtures, torch cross-checks, invariants,
+brute force).  Nothing is "parity unpinned" except the GPU's FP32
+accumulation order inside the matrix cores, which no oracle can fix; it is
+bounded by the tolerance instead.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "qlinear_oracle.c"
+_LIB = _HERE / "libqlinear_oracle.so"
+
+E4M3, E5M2, INT8 = 0, 1, 2
+IN_BF16, IN_FP32 = 0, 1
+PER_TENSOR, PER_ROW = 0, 1
+K_MAJOR, MN_MAJOR = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not _LIB.exists():
+        tmp = _LIB.with_suffix(".so.tmp%d" % os.getpid())
+        cmd = ["gcc", "-std=gnu11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", str(tmp), str(_SRC), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        build()
+    lib = ctypes.CDLL(str(_LIB))
+    i64, i32, dbl, flt, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
+    lib.orc_fp8_encode.argtypes = [dbl, i32]
+    lib.orc_fp8_encode.restype = i32
+    lib.orc_fp8_decode.argtypes = [i32, i32]
+    lib.orc_fp8_decode.restype = dbl
+    lib.orc_int8_encode.argtypes = [dbl]
+    lib.orc_int8_encode.restype = i32
+    lib.orc_div_f32.argtypes = [flt, flt]
+    lib.orc_div_f32.restype = flt
+    lib.orc_qmax.argtypes = [i32]
+    lib.orc_qmax.restype = dbl
+    lib.orc_amax_floor.argtypes = [i32]
+    lib.orc_amax_floor.restype = flt
+    lib.orc_amax_raw.argtypes = [vp, i32, i64, i64, i64, i32, vp]
+    lib.orc_amax_raw.restype = None
+    lib.orc_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, i64, vp, vp]
+    lib.orc_quantize.restype = None
+    lib.orc_qgemm_entries.argtypes = [vp, i32, i32, i64, vp, i32, i32, i64, i64, vp, vp, i64, vp, vp, vp]
+    lib.orc_qgemm_entries.restype = None
+    lib.orc_epilogue.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp]
+    lib.orc_epilogue.restype = None
+    lib.orc_fp8_output.argtypes = [vp, i64, flt, i32, vp]
+    lib.orc_fp8_output.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# scalar codecs
+
+def fp8_encode(v: float, fmt: int) -> int:
+    """sat(RNE(v)) as an E4M3/E5M2 code (OCP formats, sign of zero kept)."""
+    return _load().orc_fp8_encode(float(v), fmt)
+
+
+def fp8_decode(code: int, fmt: int) -> float:
+    """Exact value of an E4M3/E5M2 code."""
+    return _load().orc_fp8_decode(int(code), fmt)
+
+
+def int8_encode(v: float) -> int:
+    """clamp(round_half_even(v), -127, 127)."""
+    return _load().orc_int8_encode(float(v))
+
+
+def div_f32(x: float, s: float) -> np.float32:
+    """Correctly rounded FP32 quotient x/s."""
+    return np.float32(_load().orc_div_f32(float(x), float(s)))
+
+
+def qmax(fmt: int) -> float:
+    return _load().orc_qmax(fmt)
+
+
+def amax_floor(fmt: int) -> np.float32:
+    return np.float32(_load().orc_amax_floor(fmt))
+
+
+# --------------------------------------------------------------------------
+# array entry points
+
+def _input_view(x: np.ndarray):
+    """(contiguous array, dtype code) for BF16 bit patterns (uint16) or FP32."""
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), IN_BF16
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), IN_FP32
+    raise TypeError(f"oracle input must be uint16 (BF16 bits) or float32, got {x.dtype}")
+
+
+def amax_raw(x: np.ndarray, gran: int) -> np.ndarray:
+    """max|x| over the tensor ([1]) or each row ([rows]), before any floor."""
+    x2, dt = _input_view(x)
+    rows, cols = x2.shape
+    out = np.zeros(rows if gran == PER_ROW else 1, dtype=np.float64)
+    _load().orc_amax_raw(_ptr(x2), dt, rows, cols, cols, gran, _ptr(out))
+    return out
+
+
+def quantize(x: np.ndarray, gran: int, fmt: int, scale_in: np.ndarray | None = None):
+    """Return (codes uint8 [rows, cols], scale float32, amax float32).
+
+    ``x`` is a 2-D array of BF16 bit patterns (uint16) or float32.  With
+    ``scale_in`` given (delayed scaling) the codes use it; ``scale`` is then
+    still fl32(amax/qmax) of this x.
+    """
+    x2, dt = _input_view(x)
+    rows, cols = x2.shape
+    n = rows if gran == PER_ROW else 1
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scale = np.zeros(n, dtype=np.float32)
+    amax = np.zeros(n, dtype=np.float32)
+    sin = None
+    if scale_in is not None:
+        sin = np.ascontiguousarray(scale_in, dtype=np.float32)
+        if sin.size != n:
+            raise ValueError("scale_in must hold one value per scale group")
+    _load().orc_quantize(_ptr(x2), dt, rows, cols, cols, gran, fmt,
+                         _ptr(sin) if sin is not None else None,
+                         _ptr(codes), cols, _ptr(scale), _ptr(amax))
+    return codes, scale, amax
+
+
+def qgemm_entries(a: np.ndarray, a_fmt: int, a_lay: int, b: np.ndarray, b_fmt: int, b_lay: int,
+                  K: int, ms: np.ndarray, ns: np.ndarray):
+    """Exact sum_k dec(A[m,k])*dec(B[n,k]) at the listed (m, n) entries.
+
+    ``a``/``b`` are 2-D uint8 code arrays in their storage layout: K-major A
+    is [M, K] (ld = a.shape[1]), MN-major A is [K, M].  Returns
+    (acc float64, S float64, iacc int64) where S = sum_k |product| and iacc
+    is the integer sum (meaningful for INT8 x INT8).
+    """
+    a2 = np.ascontiguousarray(a, dtype=np.uint8)
+    b2 = np.ascontiguousarray(b, dtype=np.uint8)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns must have the same length")
+    cnt = ms.size
+    acc = np.zeros(cnt, dtype=np.float64)
+    sabs = np.zeros(cnt, dtype=np.float64)
+    iacc = np.zeros(cnt, dtype=np.int64)
+    _load().orc_qgemm_entries(_ptr(a2), a_fmt, a_lay, a2.shape[1], _ptr(b2), b_fmt, b_lay,
+                              b2.shape[1], K, _ptr(ms), _ptr(ns), cnt,
+                              _ptr(acc), _ptr(sabs), _ptr(iacc))
+    return acc, sabs, iacc
+
+
+def qgemm_full(a, a_fmt, a_lay, b, b_fmt, b_lay, M, N, K):
+    """All M x N entries; returns (acc [M,N], S [M,N], iacc [M,N])."""
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int64), np.arange(N, dtype=np.int64), indexing="ij")
+    acc, sabs, iacc = qgemm_entries(a, a_fmt, a_lay, b, b_fmt, b_lay, K, mm.ravel(), nn.ravel())
+    return acc.reshape(M, N), sabs.reshape(M, N), iacc.reshape(M, N)
+
+
+def epilogue(acc, ms, ns, sa, sa_gran, sb, sb_gran, bias=None):
+    """v = acc * sa * sb + bias in double, per entry."""
+    acc = np.ascontiguousarray(acc, dtype=np.float64)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    out = np.zeros(acc.size, dtype=np.float64)
+    bptr, bdt = None, 0
+    if bias is not None:
+        bias, bdt = _input_view(np.asarray(bias).reshape(1, -1))
+        bptr = _ptr(bias)
+    _load().orc_epilogue(_ptr(acc), _ptr(ms), _ptr(ns), acc.size, _ptr(sa), sa_gran,
+                         _ptr(sb), sb_gran, bptr, bdt, _ptr(out))
+    return out
+
+
+def fp8_output(v: np.ndarray, out_scale: float, fmt: int = E4M3) -> np.ndarray:
+    """sat(RNE(v / out_scale)) as FP8 codes."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    codes = np.zeros(v.size, dtype=np.uint8)
+    _load().orc_fp8_output(_ptr(v), v.size, np.float32(out_scale), fmt, _ptr(codes))
+    return codes
+
+
+def fp8_decode_array(codes: np.ndarray, fmt: int) -> np.ndarray:
+    """Exact values of an array of FP8 codes (via the 256-entry decode)."""
+    table = np.array([fp8_decode(c, fmt) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def linear_forward(x, w, bias, fmt, sx_in=None, sw_in=None, ms=None, ns=None):
+    """Quantize x [M,K] and w [N,K] per tensor, then the exact GEMM and the
+    epilogue at entries (ms, ns) (all entries when omitted).
+
+    Follows the composition in the ``linear_forward_fp8`` docstring (AstrAI
+    ops/fp8.py): quantize x and w to ``fmt``, pre-quantized GEMM with the
+    bias fused into the epilogue.  Returns a dict with codes, scales, amax,
+    acc, S and v (the reference output values, double).
+    """
+    xq, sx, ax = quantize(x, PER_TENSOR, fmt, sx_in)
+    wq, sw, aw = quantize(w, PER_TENSOR, fmt, sw_in)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if ms is None:
+        mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ms, ns = mm.ravel(), nn.ravel()
+    acc, sabs, iacc = qgemm_entries(xq, fmt, K_MAJOR, wq, fmt, K_MAJOR, K, ms, ns)
+    sx_used = sx if sx_in is None else np.asarray(sx_in, dtype=np.float32)
+    sw_used = sw if sw_in is None else np.asarray(sw_in, dtype=np.float32)
+    v = epilogue(acc, ms, ns, sx_used, PER_TENSOR, sw_used, PER_TENSOR, bias)
+    return dict(x_q=xq, sx=sx, amax_x=ax, w_q=wq, sw=sw, amax_w=aw,
+                acc=acc, S=sabs, iacc=iacc, v=v, ms=np.asarray(ms), ns=np.asarray(ns),
+                sx_used=sx_used, sw_used=sw_used)

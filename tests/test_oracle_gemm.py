@@ -1,0 +1,153 @@
+"""Pins for the oracle's GEMM and epilogue (CPU only).
+
+Definitions (cited in oracle/qlinear_oracle.c): AstrAI ops/fp8.py @5e76fbd
+``fp8_gemm``/``mm_fp8`` docstrings (a @ b * (sa*sb), FP32 accumulation, BF16
+or E4M3 output with ``out_scale`` as the output step) and the
+``linear_forward_fp8`` docstring (bias fused into the epilogue);
+scmp_kernels README "API" (a @ b.T, per_row scales).
+
+The exact accumulator is pinned against float64 / int64 library matmuls on
+inputs where those are exact, against a hand-worked fixture, and by the
+transposition and layout invariants (a transposed operand or a wrong leading
+dimension breaks them).
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+from precision_quantized_gemm_amd import synth
+
+TDT = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
+
+
+def _finite_codes(seed, stream, rows, cols, fmt, orc):
+    c = synth.random_codes(seed, stream, rows, cols)
+    if fmt == 2:
+        return np.where(c == 0x80, 0, c).astype(np.uint8)       # INT8 codes stay in [-127, 127]
+    vals = orc.fp8_decode_array(c, fmt)
+    return np.where(np.isfinite(vals), c, c & 0x70).astype(np.uint8)
+
+
+def _decode(codes, fmt):
+    if fmt == 2:
+        return codes.view(np.int8).astype(np.float64)
+    return torch.from_numpy(codes).view(TDT[fmt]).to(torch.float64).numpy()
+
+
+def test_handworked(orc):
+    g = {r[0]: r[1:] for r in read_golden("qgemm_handworked.txt")}
+    a = np.array([[int(v, 16) for v in g["a_codes"]]], dtype=np.uint8)
+    b = np.array([[int(v, 16) for v in g["b_codes"]]], dtype=np.uint8)
+    acc, S, _ = orc.qgemm_entries(a, orc.E4M3, orc.K_MAJOR, b, orc.E4M3, orc.K_MAJOR, 2, [0], [0])
+    assert acc[0] == float(g["acc"][0]) and S[0] == 4.0   # |1*3| + |2*-0.5|
+    sa = np.array([float(g["sa"][0])], np.float32)
+    sb = np.array([float(g["sb"][0])], np.float32)
+    bias = np.array([float(g["bias"][0])], np.float32)
+    v = orc.epilogue(acc, [0], [0], sa, orc.PER_TENSOR, sb, orc.PER_TENSOR, bias)
+    # BF16 of the FP32 epilogue value
+    v32 = torch.tensor(v[0], dtype=torch.float32)
+    bf = v32.to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    assert bf == int(g["bf16_out"][0], 16)
+    assert orc.fp8_output(v, float(g["out_scale"][0]))[0] == int(g["fp8_out"][0], 16)
+    ia = np.array([[int(x) for x in g["int8_a"]]], np.int8).view(np.uint8)
+    ib = np.array([[int(x) for x in g["int8_b"]]], np.int8).view(np.uint8)
+    _, _, iacc = orc.qgemm_entries(ia, orc.INT8, orc.K_MAJOR, ib, orc.INT8, orc.K_MAJOR, 2, [0], [0])
+    assert iacc[0] == int(g["int8_acc"][0])
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fp8_vs_float64_matmul(orc, fa, fb):
+    """Small K keeps every partial sum exact in float64, so the library
+    matmul of torch-decoded values must equal the oracle bit for bit."""
+    M, N, K = 7, 5, 40
+    a = _finite_codes(1, fa, M, K, fa, orc)
+    b = _finite_codes(2, fb, N, K, fb, orc)
+    A, B = _decode(a, fa), _decode(b, fb)
+    if fa == 1 and fb == 1:
+        # E5M2 x E5M2 spans 2^-32 .. 2^31.8; keep magnitudes where float64 is exact
+        a &= 0xBF
+        b &= 0xBF
+        A, B = _decode(a, fa), _decode(b, fb)
+    ref = A @ B.T
+    acc, S, _ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
+    assert np.array_equal(acc, ref)
+    assert np.array_equal(S, np.abs(A) @ np.abs(B).T)
+
+
+def test_int8_vs_int64_matmul(orc):
+    M, N, K = 9, 6, 300
+    a = _finite_codes(3, 0, M, K, 2, orc)
+    b = _finite_codes(3, 1, N, K, 2, orc)
+    ref = a.view(np.int8).astype(np.int64) @ b.view(np.int8).astype(np.int64).T
+    acc, _, iacc = orc.qgemm_full(a, orc.INT8, orc.K_MAJOR, b, orc.INT8, orc.K_MAJOR, M, N, K)
+    assert np.array_equal(iacc, ref) and np.array_equal(acc, ref.astype(np.float64))
+
+
+def test_int8_extremes(orc):
+    """K * 127^2 near the INT32 limit stays exact."""
+    K = 4096
+    a = np.full((1, K), np.int8(-127).view(np.uint8), np.uint8)
+    b = np.full((2, K), 127, np.uint8)
+    b[1, ::2] = np.int8(-127).view(np.uint8)
+    _, _, iacc = orc.qgemm_entries(a, 2, 0, b, 2, 0, K, [0, 0], [0, 1])
+    assert iacc.tolist() == [-127 * 127 * K, 0]
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (2, 2)])
+def test_transpose_and_layout_invariance(orc, fa, fb):
+    M, N, K = 11, 13, 70
+    a = _finite_codes(5, fa, M, K, fa, orc)
+    b = _finite_codes(6, fb, N, K, fb, orc)
+    acc, S, _ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
+    accT, ST, _ = orc.qgemm_full(b, fb, orc.K_MAJOR, a, fa, orc.K_MAJOR, N, M, K)
+    assert np.array_equal(acc, accT.T) and np.array_equal(S, ST.T)
+    # the same logical operands stored MN-major (k index slow)
+    aT, bT = np.ascontiguousarray(a.T), np.ascontiguousarray(b.T)
+    for la, lb, aa, bb in ((1, 0, aT, b), (0, 1, a, bT), (1, 1, aT, bT)):
+        acc2, _, _ = orc.qgemm_full(aa, fa, la, bb, fb, lb, M, N, K)
+        assert np.array_equal(acc2, acc)
+    # and the product is not symmetric in its operands (so the checks above
+    # would notice an operand read in the wrong orientation)
+    sq_a, sq_b = a[:, :K], b[:M, :K]
+    acc_ab, _, _ = orc.qgemm_full(sq_a, fa, 0, sq_b, fb, 0, M, M, K)
+    assert not np.array_equal(acc_ab, acc_ab.T)
+
+
+def test_epilogue_per_row_and_bias(orc):
+    acc = np.array([2.0, -3.0, 5.0, 7.0])
+    ms = np.array([0, 1, 0, 1])
+    ns = np.array([0, 0, 2, 2])
+    sa = np.array([0.5, 4.0], np.float32)
+    sb = np.array([2.0, 9.0, 0.25], np.float32)
+    bias = np.array([1.0, 0.0, -1.0], np.float32)
+    v = orc.epilogue(acc, ms, ns, sa, orc.PER_ROW, sb, orc.PER_ROW, bias)
+    assert v.tolist() == [2 * 0.5 * 2 + 1, -3 * 4 * 2 + 1, 5 * 0.5 * 0.25 - 1, 7 * 4 * 0.25 - 1]
+    v0 = orc.epilogue(acc, ms, ns, sa, orc.PER_TENSOR, sb, orc.PER_TENSOR, None)
+    assert v0.tolist() == [a * 0.5 * 2.0 for a in acc]
+    # BF16 bias bits
+    bb = synth.bf16_bits(torch.tensor([1.0, 0.0, -1.0]).to(torch.bfloat16))
+    vb = orc.epilogue(acc, ms, ns, sa, orc.PER_ROW, sb, orc.PER_ROW, bb)
+    assert np.array_equal(vb, v)
+
+
+def test_fp8_output_saturates_and_divides(orc):
+    v = np.array([4.2, -1000.0, 1e-9, 0.0, -0.0, 448 * 0.5])
+    codes = orc.fp8_output(v, 0.5)
+    assert codes.tolist() == [orc.fp8_encode(8.4, 0), 0xFE, 0x00, 0x00, 0x80, 0x7E]
+    ref = (torch.tensor(v[:1] / 0.5, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert codes[0] == ref.item()
+
+
+def test_linear_forward_composition(orc):
+    """Composition = quantize both operands per tensor, exact GEMM, epilogue;
+    checked against torch doing the same steps in float64."""
+    d = synth.workload("tiny_linear")
+    x, w, bias = synth.bf16_bits(d["x"]), synth.bf16_bits(d["w"]), d["bias"].numpy()
+    r = orc.linear_forward(x, w, bias, orc.E4M3)
+    X = _decode(r["x_q"], 0)
+    W = _decode(r["w_q"], 0)
+    ref = (X @ W.T) * np.float64(r["sx"][0]) * np.float64(r["sw"][0]) + bias.astype(np.float64)
+    # float64 matmul of K=128 E4M3 products is exact; the scaling then rounds once
+    assert np.allclose(r["v"].reshape(512, 128), ref, rtol=1e-15, atol=0)
+    assert r["amax_x"][0] == d["x"].float().abs().max().item()

@@ -1,0 +1,182 @@
+"""Pins for the oracle's quantize (CPU only).
+
+Definitions followed by the oracle (cited in oracle/qlinear_oracle.c):
+AstrAI ops/fp8.py @5e76fbd (``_fp8_quantize_cpu``, ``quantize_bf16``
+docstring) and POPCORNBENCH "Kimi-K2.6 l2_p13" (reference-model steps 2-4).
+Pinned here by hand-worked fixtures, by torch's own FP32 division and casts
+(independent implementations of the same printed formulas, compared where
+torch and the saturating contract agree), and by invariants that a dropped
+term, a wrong sign or a wrong index would break.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+from precision_quantized_gemm_amd import synth
+
+TDT = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
+QMAX = {0: 448.0, 1: 57344.0, 2: 127.0}
+
+
+def _bf16(vals):
+    return synth.bf16_bits(torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16))
+
+
+def test_handworked_fp8(orc):
+    rows = list(read_golden("quantize_fp8_handworked.txt"))
+    vals = [float(r[1]) for r in rows]
+    # the BF16 rounding of each decimal is the second column
+    for r in rows:
+        dec = eval(r[0].replace("^", "**"))
+        assert float(torch.tensor(dec).to(torch.bfloat16)) == float(r[1])
+    x = _bf16(vals).reshape(1, -1)
+    codes, scale, amax = orc.quantize(x, orc.PER_TENSOR, orc.E4M3)
+    assert amax[0] == 448.0 and scale[0] == 1.0
+    assert [int(c) for c in codes[0]] == [int(r[2], 16) for r in rows]
+    codes5, _, _ = orc.quantize(x, orc.PER_TENSOR, orc.E5M2, np.array([1.0], np.float32))
+    assert [int(c) for c in codes5[0]] == [int(r[3], 16) for r in rows]
+
+
+def test_handworked_int8_per_row(orc):
+    g = {}
+    for r in read_golden("int8_perrow_handworked.txt"):
+        g.setdefault(r[0], []).append([float(v) for v in r[1:]])
+    a = np.array(g["a"], dtype=np.float32)
+    b = np.array(g["b"], dtype=np.float32)
+    qa, sa, _ = orc.quantize(a, orc.PER_ROW, orc.INT8)
+    qb, sb, _ = orc.quantize(b, orc.PER_ROW, orc.INT8)
+    assert list(sa) == g["sa"][0] and list(sb) == g["sb"][0]
+    assert qa.view(np.int8).tolist() == [[int(v) for v in row] for row in g["qa"]]
+    assert qb.view(np.int8).tolist() == [[int(v) for v in row] for row in g["qb"]]
+
+
+def _torch_fp8_reference(x32, scale, fmt):
+    """AstrAI's CPU definition (x.float()/scale cast to fp8) run in torch."""
+    return (torch.from_numpy(x32) / torch.tensor(scale, dtype=torch.float32)).to(TDT[fmt]).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -5, 3.3 / 448, 7.0 / 127, 0.0137])
+def test_all_bf16_vs_torch_cast(orc, fmt, scale):
+    """Every finite BF16 input x with |x/scale| below the format max: the
+    oracle's codes equal torch's division + cast (which rounds to even)."""
+    scale = np.float32(scale)
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    x32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    keep = np.isfinite(x32)
+    q = (torch.from_numpy(x32[keep]) / torch.tensor(scale)).numpy()
+    keep[keep] = np.abs(q) < QMAX[fmt]
+    bits, x32 = bits[keep], x32[keep]
+    codes, _, _ = orc.quantize(bits.reshape(1, -1), orc.PER_TENSOR, fmt, np.array([scale]))
+    ref = _torch_fp8_reference(x32, scale, fmt)
+    assert np.array_equal(codes[0], ref)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0137, 7.0 / 127, 2.0 ** -3])
+def test_int8_vs_torch_formula(orc, scale):
+    """POPCORNBENCH steps 3-4 written in torch: clamp(round(x/scale), +-127)."""
+    scale = np.float32(scale)
+    x = synth.random_fp32(11, 0, 64, 1024, std=1.5).numpy()
+    codes, _, _ = orc.quantize(x, orc.PER_TENSOR, orc.INT8, np.array([scale]))
+    ref = torch.clamp(torch.round(torch.from_numpy(x) / torch.tensor(scale)), -127, 127)
+    assert np.array_equal(codes.view(np.int8).astype(np.int64), ref.numpy().astype(np.int64))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_current_scaling_amax_and_scale(orc, fmt, dt):
+    t = synth.random_bf16(5, fmt, 33, 77) if dt == "bf16" else synth.random_fp32(5, fmt, 33, 77)
+    x = synth.bf16_bits(t) if dt == "bf16" else t.numpy()
+    tf = t.float()
+    codes, scale, amax = orc.quantize(x, orc.PER_TENSOR, fmt)
+    floor = np.float32(1e-8 if fmt == 2 else 1e-12)
+    ref_amax = tf.abs().amax().clamp_min(float(floor))
+    assert amax[0] == np.float32(ref_amax.item())
+    assert scale[0] == np.float32((ref_amax / QMAX[fmt]).item())
+    # per row
+    codes_r, scale_r, amax_r = orc.quantize(x, orc.PER_ROW, fmt)
+    ref_rows = tf.abs().amax(dim=1).clamp_min(float(floor))
+    assert np.array_equal(amax_r, ref_rows.numpy())
+    assert np.array_equal(scale_r, (ref_rows / QMAX[fmt]).numpy())
+    # current scaling == delayed scaling with the same scales
+    again, _, _ = orc.quantize(x, orc.PER_ROW, fmt, scale_r)
+    assert np.array_equal(again, codes_r)
+    # the largest element saturates exactly to qmax
+    i = int(np.argmax(np.abs(tf.numpy()).ravel()))
+    c = int(codes.ravel()[i])
+    if fmt == 2:
+        assert abs(int(np.array([c], np.uint8).view(np.int8)[0])) == 127
+    else:
+        assert orc.fp8_decode(c, fmt) in (QMAX[fmt], -QMAX[fmt])
+
+
+def test_amax_floor(orc):
+    z = np.zeros((3, 5), dtype=np.float32)
+    for fmt, floor in ((0, 1e-12), (1, 1e-12), (2, 1e-8)):
+        codes, scale, amax = orc.quantize(z, orc.PER_TENSOR, fmt)
+        assert amax[0] == np.float32(floor)
+        assert scale[0] == np.float32(np.float32(floor) / np.float32(QMAX[fmt]))
+        assert not codes.any()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_invariants(orc, fmt):
+    x = synth.random_fp32(9, 1, 16, 96).numpy()
+    codes, scale, amax = orc.quantize(x, orc.PER_TENSOR, fmt)
+    # power-of-two homogeneity: codes unchanged, scale and amax scale by 2^j
+    for j in (-7, 5):
+        c2, s2, a2 = orc.quantize((x * np.float32(2.0 ** j)).astype(np.float32), orc.PER_TENSOR, fmt)
+        assert np.array_equal(c2, codes)
+        assert s2[0] == scale[0] * np.float32(2.0 ** j) and a2[0] == amax[0] * np.float32(2.0 ** j)
+    # sign symmetry
+    cn, sn, _ = orc.quantize(-x, orc.PER_TENSOR, fmt)
+    assert sn[0] == scale[0]
+    if fmt == 2:
+        assert np.array_equal(cn.view(np.int8), -codes.view(np.int8))
+    else:
+        assert np.array_equal(cn, codes ^ 0x80)
+    # permutation of the elements permutes the codes, amax unchanged
+    perm = synth.permutation(9, 2, x.size)
+    cp, sp, ap = orc.quantize(x.ravel()[perm].reshape(x.shape), orc.PER_TENSOR, fmt)
+    assert ap[0] == amax[0] and np.array_equal(cp.ravel(), codes.ravel()[perm])
+    # per-row equals per-tensor when every row has the same amax
+    xr = x.copy()
+    xr[:, 0] = np.float32(amax[0])
+    cr, sr, ar = orc.quantize(xr, orc.PER_ROW, fmt)
+    ct, st, at = orc.quantize(xr, orc.PER_TENSOR, fmt)
+    assert np.all(sr == st[0]) and np.array_equal(cr, ct)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_dequant_identity(orc, fmt):
+    """|dec(q)*scale - x| <= half a step of the format at v (unsaturated)."""
+    x = synth.random_fp32(21, fmt, 64, 256, std=2.0).numpy()
+    codes, scale, _ = orc.quantize(x, orc.PER_TENSOR, fmt)
+    s = float(scale[0])
+    v = x.astype(np.float64) / s
+    if fmt == 2:
+        deq = codes.view(np.int8).astype(np.float64)
+        err = np.abs(deq - v)
+        assert err.max() <= 0.5 + 1e-6
+        return
+    deq = orc.fp8_decode_array(codes, fmt)
+    mbits, emin = (3, -6) if fmt == 0 else (2, -14)
+    e = np.maximum(np.floor(np.log2(np.maximum(np.abs(v), 1e-300))), emin)
+    half_ulp = 0.5 * 2.0 ** (e - mbits)
+    # the FP32 quotient adds at most half an FP32 ulp
+    assert np.all(np.abs(deq - v) <= half_ulp * (1 + 1e-6) + np.abs(v) * 2.0 ** -24)
+
+
+def test_row_index_and_leading_dim(orc):
+    """Rows are quantized with their own scale: swapping two rows swaps the
+    codes and scales (a wrong row index would break this)."""
+    x = synth.random_fp32(31, 0, 5, 40).numpy()
+    x[2] *= 9
+    c, s, a = orc.quantize(x, orc.PER_ROW, orc.E4M3)
+    xs = x[[2, 1, 0, 3, 4]]
+    c2, s2, a2 = orc.quantize(xs, orc.PER_ROW, orc.E4M3)
+    assert np.array_equal(c2, c[[2, 1, 0, 3, 4]]) and np.array_equal(s2, s[[2, 1, 0, 3, 4]])
+    assert s[2] > 4 * s[1]
