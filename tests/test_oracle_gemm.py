@@ -39,7 +39,7 @@ def test_handworked(orc):
     g = {r[0]: r[1:] for r in read_golden("qgemm_handworked.txt")}
     a = np.array([[int(v, 16) for v in g["a_codes"]]], dtype=np.uint8)
     b = np.array([[int(v, 16) for v in g["b_codes"]]], dtype=np.uint8)
-    acc, S, _ = orc.qgemm_entries(a, orc.E4M3, orc.K_MAJOR, b, orc.E4M3, orc.K_MAJOR, 2, [0], [0])
+    acc, S, _, *_ = orc.qgemm_entries(a, orc.E4M3, orc.K_MAJOR, b, orc.E4M3, orc.K_MAJOR, 2, [0], [0])
     assert acc[0] == float(g["acc"][0]) and S[0] == 4.0   # |1*3| + |2*-0.5|
     sa = np.array([float(g["sa"][0])], np.float32)
     sb = np.array([float(g["sb"][0])], np.float32)
@@ -52,7 +52,7 @@ def test_handworked(orc):
     assert orc.fp8_output(v, float(g["out_scale"][0]))[0] == int(g["fp8_out"][0], 16)
     ia = np.array([[int(x) for x in g["int8_a"]]], np.int8).view(np.uint8)
     ib = np.array([[int(x) for x in g["int8_b"]]], np.int8).view(np.uint8)
-    _, _, iacc = orc.qgemm_entries(ia, orc.INT8, orc.K_MAJOR, ib, orc.INT8, orc.K_MAJOR, 2, [0], [0])
+    _, _, iacc, *_ = orc.qgemm_entries(ia, orc.INT8, orc.K_MAJOR, ib, orc.INT8, orc.K_MAJOR, 2, [0], [0])
     assert iacc[0] == int(g["int8_acc"][0])
 
 
@@ -70,7 +70,7 @@ def test_fp8_vs_float64_matmul(orc, fa, fb):
         b &= 0xBF
         A, B = _decode(a, fa), _decode(b, fb)
     ref = A @ B.T
-    acc, S, _ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
+    acc, S, _, *_ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
     assert np.array_equal(acc, ref)
     assert np.array_equal(S, np.abs(A) @ np.abs(B).T)
 
@@ -80,7 +80,7 @@ def test_int8_vs_int64_matmul(orc):
     a = _finite_codes(3, 0, M, K, 2, orc)
     b = _finite_codes(3, 1, N, K, 2, orc)
     ref = a.view(np.int8).astype(np.int64) @ b.view(np.int8).astype(np.int64).T
-    acc, _, iacc = orc.qgemm_full(a, orc.INT8, orc.K_MAJOR, b, orc.INT8, orc.K_MAJOR, M, N, K)
+    acc, _, iacc, *_ = orc.qgemm_full(a, orc.INT8, orc.K_MAJOR, b, orc.INT8, orc.K_MAJOR, M, N, K)
     assert np.array_equal(iacc, ref) and np.array_equal(acc, ref.astype(np.float64))
 
 
@@ -90,7 +90,7 @@ def test_int8_extremes(orc):
     a = np.full((1, K), np.int8(-127).view(np.uint8), np.uint8)
     b = np.full((2, K), 127, np.uint8)
     b[1, ::2] = np.int8(-127).view(np.uint8)
-    _, _, iacc = orc.qgemm_entries(a, 2, 0, b, 2, 0, K, [0, 0], [0, 1])
+    _, _, iacc, *_ = orc.qgemm_entries(a, 2, 0, b, 2, 0, K, [0, 0], [0, 1])
     assert iacc.tolist() == [-127 * 127 * K, 0]
 
 
@@ -99,18 +99,18 @@ def test_transpose_and_layout_invariance(orc, fa, fb):
     M, N, K = 11, 13, 70
     a = _finite_codes(5, fa, M, K, fa, orc)
     b = _finite_codes(6, fb, N, K, fb, orc)
-    acc, S, _ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
-    accT, ST, _ = orc.qgemm_full(b, fb, orc.K_MAJOR, a, fa, orc.K_MAJOR, N, M, K)
+    acc, S, _, *_ = orc.qgemm_full(a, fa, orc.K_MAJOR, b, fb, orc.K_MAJOR, M, N, K)
+    accT, ST, _, *_ = orc.qgemm_full(b, fb, orc.K_MAJOR, a, fa, orc.K_MAJOR, N, M, K)
     assert np.array_equal(acc, accT.T) and np.array_equal(S, ST.T)
     # the same logical operands stored MN-major (k index slow)
     aT, bT = np.ascontiguousarray(a.T), np.ascontiguousarray(b.T)
     for la, lb, aa, bb in ((1, 0, aT, b), (0, 1, a, bT), (1, 1, aT, bT)):
-        acc2, _, _ = orc.qgemm_full(aa, fa, la, bb, fb, lb, M, N, K)
+        acc2, _, _, *_ = orc.qgemm_full(aa, fa, la, bb, fb, lb, M, N, K)
         assert np.array_equal(acc2, acc)
     # and the product is not symmetric in its operands (so the checks above
     # would notice an operand read in the wrong orientation)
     sq_a, sq_b = a[:, :K], b[:M, :K]
-    acc_ab, _, _ = orc.qgemm_full(sq_a, fa, 0, sq_b, fb, 0, M, M, K)
+    acc_ab, _, _, *_ = orc.qgemm_full(sq_a, fa, 0, sq_b, fb, 0, M, M, K)
     assert not np.array_equal(acc_ab, acc_ab.T)
 
 
@@ -151,3 +151,29 @@ def test_linear_forward_composition(orc):
     # float64 matmul of K=128 E4M3 products is exact; the scaling then rounds once
     assert np.allclose(r["v"].reshape(512, 128), ref, rtol=1e-15, atol=0)
     assert r["amax_x"][0] == d["x"].float().abs().max().item()
+
+
+def test_truncation_bound_H(orc):
+    """H counts one grid step 2^(max(e_a+e_b) - 13) per product that is not
+    on the grid of its aligned group of 8 consecutive k."""
+    one, tiny = 0x3C, 0x04          # E5M2: 1.0 and 2^-14 (e = -14)
+    a = np.zeros((1, 16), np.uint8)
+    a[0, 0] = one
+    a[0, 1:8] = tiny                # group 0: big 1*1 (e=0) + seven 2^-14 products
+    a[0, 8:16] = tiny               # group 1: only small products, all on their grid
+    b = np.full((1, 16), one, np.uint8)
+    acc, S, _, H = orc.qgemm_entries(a, 1, 0, b, 1, 0, 16, [0], [0])
+    assert acc[0] == 1 + 15 * 2.0 ** -14
+    assert H[0] == 7 * 2.0 ** -13
+    # all products integers on a coarse grid: nothing truncated
+    ai = np.array([[orc.fp8_encode(v, 0) for v in (1, 2, 3, -4, 5, 6, 7, 8)]], np.uint8)
+    bi = np.array([[orc.fp8_encode(v, 0) for v in (8, 7, -6, 5, 4, 3, 2, 1)]], np.uint8)
+    _, _, _, H2 = orc.qgemm_entries(ai, 0, 0, bi, 0, 0, 8, [0], [0])
+    assert H2[0] == 0.0
+    # INT8 products are exact integers
+    _, _, _, H3 = orc.qgemm_entries(ai, 2, 0, bi, 2, 0, 8, [0], [0])
+    assert H3[0] == 0.0
+    # a product is on the grid of its own group only: move the big term away
+    a2 = a.copy(); a2[0, 0] = 0
+    _, _, _, H4 = orc.qgemm_entries(a2, 1, 0, b, 1, 0, 16, [0], [0])
+    assert H4[0] == 0.0
