@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear layer on one MI355X.
+
+One step = the whole hot path on the large FP8 workload
+(a BF16 [16384, 8192] ~ Student-t(3), b BF16 [8192, 8192] ~ N(0, 1/8192)):
+per-tensor E4M3 quantize of a and of b (amax reduction, on-device step,
+cast), then the scaled E4M3 GEMM 16384 x 8192 x 8192 with FP32 accumulation
+and E4M3 output (out_scale = amax_prev / 448, amax_prev being the out_amax
+of the previous step on the same inputs), which also publishes the step's
+own out_amax.  That is one ql_linear_forward call.
+
+Prints one JSON line.  `value` is the step's GEMM work (2*M*N*K) divided by
+the step time (inputs resident in HBM).  `roofline` is the GEMM kernel alone
+against the dense FP8 matrix-core peak, timed with HIP events on the stream
+it is launched on; `quantize` reports the quantize kernels against HBM
+peak; `cpu_baseline` is the oracle (plain C) timed on a bounded sample of
+the same workload on this host's cores and scaled to the full step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "qgemm TFLOP/s & % dense FP8/INT8 MFMA peak; quantize GB/s & % HBM peak"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 matrix-core peak
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=30, help="launches per per-kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4, help="output rows in the oracle GEMM sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_events(fn, reps, torch):
+    """Average milliseconds per call of fn over `reps` back-to-back calls,
+    measured with events on torch's current stream (where fn launches)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(a_cpu, b_cpu, M, N, K, rows):
+    """Oracle timing on a bounded sample, scaled to one full step.
+
+    Sample: the per-tensor E4M3 quantize of `rows_q` rows of a and of b, and
+    the exact GEMM of `rows` full output rows (rows x N entries x K), split
+    over the host's threads.  Step estimate = per-element quantize time x
+    (M*K + N*K) + per-MAC GEMM time x M*N*K.
+    """
+    import numpy as np
+
+    import oracle
+    from precision_quantized_gemm_amd import synth
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows_q = 256
+    xa = synth.bf16_bits(a_cpu[:rows_q])
+    xb = synth.bf16_bits(b_cpu[:rows_q])
+    t0 = time.perf_counter()
+    qa, sa, _ = oracle.quantize(xa, oracle.PER_TENSOR, oracle.E4M3)
+    qb, sb, _ = oracle.quantize(xb, oracle.PER_TENSOR, oracle.E4M3)
+    tq = (time.perf_counter() - t0) / (2 * rows_q * K)
+    # GEMM sample: `rows` output rows against the first rows_q rows of b
+    # (the per-entry cost does not depend on which rows are used).
+    ms = np.repeat(np.arange(rows), rows_q).astype(np.int64)
+    ns = np.tile(np.arange(rows_q), rows).astype(np.int64)
+    chunks = np.array_split(np.arange(ms.size), threads)
+
+    def work(idx):
+        oracle.qgemm_entries(qa, 0, 0, qb, 0, 0, K, ms[idx], ns[idx], with_bound=False)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as pool:
+        list(pool.map(work, chunks))
+    tg_wall = time.perf_counter() - t0
+    tmac = tg_wall / (ms.size * K)
+    step_s = tq * (M * K + N * K) + tmac * M * N * K
+    return dict(value=2.0 * M * N * K / step_s / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=(f"quantize of {rows_q} rows of a and of b ({2 * rows_q * K} elements, 1 thread) and the "
+                        f"exact GEMM of {rows}x{rows_q} outputs x K={K} ({ms.size * K} MACs, {threads} threads); "
+                        f"scaled to the full {M}x{N}x{K} step"),
+                step_seconds_estimate=step_s)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_quantized_gemm_amd as q
+    from precision_quantized_gemm_amd import _lib, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs")
+    d = synth.workload("large_fp8")
+    a_cpu, b_cpu = d["a"], d["b"]
+    M, K = a_cpu.shape
+    N = b_cpu.shape[0]
+    a = a_cpu.to(dev)
+    b = b_cpu.to(dev)
+    u8 = torch.uint8
+    out = torch.empty((M, N), dtype=u8, device=dev)
+    x_q = torch.empty((M, K), dtype=u8, device=dev)
+    w_q = torch.empty((N, K), dtype=u8, device=dev)
+    f1 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
+    sx, amax_x, sw, amax_w, out_amax = f1(), f1(), f1(), f1(), f1()
+    out_scale = torch.ones(1, dtype=torch.float32, device=dev)
+    ws = q.new_workspace(dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def step():
+        q.ql_linear_forward(P(a), _lib.QL_DT_BF16, M, K, P(b), N, None, 0, _lib.QL_FMT_E4M3, None, None,
+                            P(out), _lib.QL_DT_E4M3, P(out_scale), P(out_amax), P(x_q), P(sx), P(amax_x),
+                            P(w_q), P(sw), P(amax_w), P(ws), stream)
+
+    def gemm_only():
+        q.ql_qgemm(P(x_q), 0, 0, K, P(w_q), 0, 0, K, M, N, K, P(sx), 0, P(sw), 0, None, 0,
+                   P(out), _lib.QL_DT_E4M3, N, P(out_scale), None, P(ws), stream)
+
+    def quant(x, rows, xq, s, am):
+        return lambda: q.ql_quantize(P(x), _lib.QL_DT_BF16, rows, K, K, 0, 0, None, P(xq), K, P(s), P(am),
+                                     P(ws), stream)
+
+    log("warmup")
+    step()
+    torch.cuda.synchronize()
+    out_scale.copy_(out_amax / 448.0)           # amax_prev / 448
+    for _ in range(max(0, args.warmup - 1)):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ms_step = time_events(step, args.steps, torch)
+    t_wall = time.perf_counter() - t_wall0
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    log("per-kernel timing")
+    ms_gemm = time_events(gemm_only, args.kernel_reps, torch)
+    ms_qa = time_events(quant(a, M, x_q, sx, amax_x), args.kernel_reps, torch)
+    ms_qb = time_events(quant(b, N, w_q, sw, amax_w), args.kernel_reps, torch)
+    gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
+    # quantize traffic: per-tensor current scaling reads x twice (amax pass,
+    # cast pass) and writes 1 byte per element: 5 B/elem of BF16 input; the
+    # compulsory traffic is 3 B/elem.
+    qa_bytes5, qa_bytes3 = 5.0 * M * K, 3.0 * M * K
+    qb_bytes5 = 5.0 * N * K
+    qa_gbps = qa_bytes5 / (ms_qa * 1e-3) / 1e9
+    qb_gbps = qb_bytes5 / (ms_qb * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(a_cpu, b_cpu, M, N, K, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "large_fp8: quantize a[16384,8192] bf16 Student-t(3) and b[8192,8192] bf16 N(0,1/8192) "
+                        "per-tensor E4M3, then E4M3 GEMM 16384x8192x8192 FP32-acc, E4M3 out "
+                        "(out_scale = amax_prev/448), one ql_linear_forward per step",
+            "M": M, "N": N, "K": K, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "qgemm_kernel<E4M3,E4M3,K-major,K-major,256x256>",
+            "ms_per_launch": round(ms_gemm, 5),
+        },
+        "quantize": {
+            "a_ms": round(ms_qa, 5), "b_ms": round(ms_qb, 5),
+            "a_GBps_5B_per_elem": round(qa_gbps, 1),
+            "a_GBps_3B_per_elem": round(qa_bytes3 / (ms_qa * 1e-3) / 1e9, 1),
+            "b_GBps_5B_per_elem": round(qb_gbps, 1),
+            "a_frac_hbm_peak_5B": round(qa_gbps / PEAK_HBM_GBPS, 4),
+            "peak_GBps": PEAK_HBM_GBPS,
+        },
+        "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
+                                                 for k, v in cpu.items()},
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

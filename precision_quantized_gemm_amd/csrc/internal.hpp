@@ -1,0 +1,66 @@
+// internal.hpp -- parameter blocks and launchers shared between the C-ABI
+// front end (qlinear_api.cpp) and the kernel files.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+// Workspace layout: slots of 256 bytes, each {amax bits, counter, ...}.
+constexpr int64_t WS_SLOT_BYTES = 256;
+constexpr int64_t WS_SLOT_QA = 0;      // quantize of x / A
+constexpr int64_t WS_SLOT_QB = 1;      // quantize of w / B (linear_forward)
+constexpr int64_t WS_SLOT_GEMM = 2;    // GEMM output amax
+constexpr int64_t WS_BYTES = 4 * WS_SLOT_BYTES;
+
+inline uint32_t *ws_slot(void *ws, int64_t slot)
+{
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + slot * WS_SLOT_BYTES);
+}
+
+struct QzParams {
+    const void *x;
+    int64_t rows, cols, ldx;
+    void *xq;
+    int64_t ldq;
+    const float *scale_src;   // step the cast uses: scale_out (current) or scale_in (delayed)
+    float *scale_out;         // fl32(amax / qmax)
+    float *amax_out;
+    uint32_t *ws;             // workspace slot (per-tensor only)
+    float qmax, floor;
+    int64_t n_elems;          // rows * cols
+    int64_t n_units;          // 16-element vector units (flat / rows modes)
+    int64_t units_per_row;    // cols / 16 (rows mode, per-row vector path)
+    int mode;                 // 0 flat-vector, 1 rows-vector, 2 scalar
+    int per_row;
+    int vec_rows;             // per-row kernel may use 16-byte units
+    int delayed;
+};
+
+hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s);
+hipError_t launch_ws_zero(void *ws, int64_t bytes, hipStream_t s);
+
+struct GemmParams {
+    const uint8_t *a, *b;
+    int64_t lda, ldb;
+    int64_t M, N, K;
+    const float *sa, *sb;
+    int64_t sa_stride, sb_stride;   // 0 (per tensor) or 1 (per row)
+    const void *bias;
+    int bias_dt;                    // -1 none, 0 BF16, 1 FP32
+    void *out;
+    int64_t ldo;
+    int out_dt;                     // DT_BF16 / DT_FP32 / DT_E4M3 / DT_INT32
+    const float *out_scale;
+    float *out_amax;
+    uint32_t *ws;                   // workspace slot for out_amax
+    int a_aligned, b_aligned;       // 16-byte loads allowed
+    int out_vec4;                   // 4 consecutive outputs may be stored as one vector
+    int tiles_m, tiles_n;
+};
+
+// a_fmt / b_fmt: FMT_*; a_mn / b_mn: operand stored MN-major.
+hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s);
+
+}  // namespace ql

@@ -1,0 +1,12 @@
+// qgemm_e4m3_e4m3.hip -- instantiations of the scaled GEMM for A in FMT_E4M3 and B in
+// FMT_E4M3 (one file per format pair so the build compiles them in parallel).
+#include "qgemm_impl.hpp"
+
+namespace ql {
+
+hipError_t launch_qgemm_e4m3_e4m3(const GemmParams &p, int a_mn, int b_mn, hipStream_t s)
+{
+    return launch_formats<FMT_E4M3, FMT_E4M3>(p, a_mn, b_mn, s);
+}
+
+}  // namespace ql

@@ -1,0 +1,12 @@
+// qgemm_e5m2_e5m2.hip -- instantiations of the scaled GEMM for A in FMT_E5M2 and B in
+// FMT_E5M2 (one file per format pair so the build compiles them in parallel).
+#include "qgemm_impl.hpp"
+
+namespace ql {
+
+hipError_t launch_qgemm_e5m2_e5m2(const GemmParams &p, int a_mn, int b_mn, hipStream_t s)
+{
+    return launch_formats<FMT_E5M2, FMT_E5M2>(p, a_mn, b_mn, s);
+}
+
+}  // namespace ql

@@ -1,0 +1,388 @@
+// qgemm_impl.hpp -- scaled FP8 / INT8 matrix-core GEMM for gfx950.
+//
+//   out[m, n] = (sum_k A[m, k] * B[n, k]) * sa[m|0] * sb[n|0] (+ bias[n])
+//
+// AstrAI ops/fp8.py @5e76fbd: fp8_gemm / mm_fp8 (a @ b * (sa*sb), FP32
+// accumulation, BF16 or E4M3 output where E4M3 divides by out_scale, the
+// output quantization step) and linear_forward_fp8 (bias fused into the GEMM
+// epilogue); scmp_kernels README "API" (a @ b.T, per-row scales).
+//
+// Design (one workgroup = 4 waves = one BM x BN output tile):
+//   * K advances in steps of 128 bytes.  Each step's A and B tiles are
+//     staged in LDS, double buffered: the global loads of step k+1 are in
+//     flight while the matrix cores work on step k.
+//   * LDS holds every operand K-major (128 bytes per row) with a 16-byte
+//     chunk swizzle, so the fragment reads (one row per lane, two 16-byte
+//     chunks) are free of bank conflicts.  MN-major operands are transposed
+//     in registers (byte shuffles) on their way into LDS.
+//   * FP8: v_mfma_f32_16x16x128_f8f6f4 with per-operand formats (E4M3 and
+//     E5M2 mix freely).  INT8: two v_mfma_i32_16x16x64_i8 per 128 bytes,
+//     exact in INT32.  Each lane's 32 fragment bytes are 32 consecutive k, so
+//     the matrix core's groups of 8 products are 8 consecutive k.
+//   * Tile order: tiles are grouped GM tile-rows at a time so a run of
+//     workgroups shares A rows and B columns, and consecutive tiles of that
+//     order are placed on the same XCD (workgroup ids go round-robin over
+//     the 8 XCDs, each with its own L2).  This is the gfx950 form of the
+//     grouped rasterization the AstrAI commit message describes.
+//   * Epilogue: scale, bias and the output cast fused; optional max|v| of
+//     the output published by the last workgroup (same election as the
+//     quantize reduction).
+#pragma once
+
+#include "qdev.hpp"
+#include "internal.hpp"
+
+namespace ql {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int GEMM_BK = 128;
+constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_GM = 8;   // tile-rows per group in the tile order
+
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 7); }
+__device__ __forceinline__ int lds_off(int r, int chunk) { return r * GEMM_BK + ((chunk ^ lds_swz(r)) << 4); }
+
+// Load up to 16 bytes [p, p + n) into a zero-padded 16-byte vector.
+__device__ __forceinline__ uint4 load_partial(const uint8_t *p, int64_t n)
+{
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (i < n) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// Stage one K step of one operand ([ROWS, 128 bytes] of the logical [MN, K]
+// matrix) from global memory into registers, then into LDS.
+template <int ROWS, bool MN_MAJOR> struct Stage;
+
+// K-major: 8 threads read one row's 128 contiguous bytes.
+template <int ROWS> struct Stage<ROWS, false> {
+    static constexpr int PER = ROWS * 8 / GEMM_THREADS;
+    uint4 r[PER];
+    __device__ __forceinline__ void load(const uint8_t *base, int64_t ld, int64_t row0, int64_t rows_total,
+                                         int64_t k0, int64_t K, bool aligned)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = i * GEMM_THREADS + (int)threadIdx.x;
+            const int64_t grow = row0 + (c >> 3);
+            const int64_t gk = k0 + (c & 7) * 16;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (grow < rows_total && gk < K) {
+                const uint8_t *src = base + grow * ld + gk;
+                if (aligned && gk + 16 <= K) v = *reinterpret_cast<const uint4 *>(src);
+                else v = load_partial(src, K - gk);
+            }
+            r[i] = v;
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = i * GEMM_THREADS + (int)threadIdx.x;
+            *reinterpret_cast<uint4 *>(lds + lds_off(c >> 3, c & 7)) = r[i];
+        }
+    }
+};
+
+// MN-major (storage [K][MN]): a thread reads 8 k-rows x 16 mn-bytes and
+// transposes them to 16 rows of 8 consecutive k.
+template <int ROWS> struct Stage<ROWS, true> {
+    static constexpr int GROUPS = ROWS / 16;                     // 16-byte mn groups
+    static constexpr int UNITS = GROUPS * (GEMM_BK / 8);         // = ROWS
+    static constexpr int PER = (UNITS + GEMM_THREADS - 1) / GEMM_THREADS;
+    uint4 r[PER][8];
+    __device__ __forceinline__ void load(const uint8_t *base, int64_t ld, int64_t row0, int64_t rows_total,
+                                         int64_t k0, int64_t K, bool aligned)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = i * GEMM_THREADS + (int)threadIdx.x;
+            const int mg = u % GROUPS, kq = u / GROUPS;
+            const int64_t mn = row0 + mg * 16;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t k = k0 + kq * 8 + j;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (u < UNITS && k < K && mn < rows_total) {
+                    const uint8_t *src = base + k * ld + mn;
+                    if (aligned && mn + 16 <= rows_total) v = *reinterpret_cast<const uint4 *>(src);
+                    else v = load_partial(src, rows_total - mn);
+                }
+                r[i][j] = v;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = i * GEMM_THREADS + (int)threadIdx.x;
+            if (u >= UNITS) continue;
+            const int mg = u % GROUPS, kq = u / GROUPS;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int w = e >> 2, sh = (e & 3) * 8;
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    lo |= ((word_of(r[i][j], w) >> sh) & 0xFFu) << (8 * j);
+                    hi |= ((word_of(r[i][j + 4], w) >> sh) & 0xFFu) << (8 * j);
+                }
+                const int row = mg * 16 + e;
+                *reinterpret_cast<uint2 *>(lds + lds_off(row, kq >> 1) + (kq & 1) * 8) = make_uint2(lo, hi);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+template <int AF, int BF> struct Mma {
+    typedef v4f acc_t;
+    __device__ __forceinline__ static void run(acc_t &c, const v8i &a, const v8i &b)
+    {
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
+    }
+    static constexpr bool INT_ACC = false;
+    __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return __float_as_uint(c[r]); }
+};
+
+template <> struct Mma<FMT_INT8, FMT_INT8> {
+    typedef v4i acc_t;
+    __device__ __forceinline__ static void run(acc_t &c, const v8i &a, const v8i &b)
+    {
+        v4i a0 = {a[0], a[1], a[2], a[3]}, a1 = {a[4], a[5], a[6], a[7]};
+        v4i b0 = {b[0], b[1], b[2], b[3]}, b1 = {b[4], b[5], b[6], b[7]};
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c, 0, 0, 0);
+    }
+    static constexpr bool INT_ACC = true;
+    __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return (uint32_t)c[r]; }
+};
+
+// Fragment of 16 rows x 32 k for lane l: row (l & 15), k = 32*(l >> 4) .. +31.
+__device__ __forceinline__ v8i load_frag(const uint8_t *lds, int row, int g)
+{
+    uint4 x = *reinterpret_cast<const uint4 *>(lds + lds_off(row, 2 * g));
+    uint4 y = *reinterpret_cast<const uint4 *>(lds + lds_off(row, 2 * g + 1));
+    v8i f = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    return f;
+}
+
+// Fused epilogue for 4 consecutive outputs of one row:
+//   v = acc * sa[row|0] * sb[col|0] (+ bias[col]), then the output cast.
+struct Epilogue {
+    const GemmParams &p;
+    Divider odiv;
+    __device__ __forceinline__ explicit Epilogue(const GemmParams &pp)
+        : p(pp), odiv(pp.out_dt == DT_E4M3 ? pp.out_scale[0] : 1.0f) {}
+
+    __device__ __forceinline__ float bias_at(int64_t col) const
+    {
+        if (p.bias_dt == DT_FP32) return static_cast<const float *>(p.bias)[col];
+        if (p.bias_dt == DT_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p.bias)[col] << 16);
+        return 0.0f;
+    }
+
+    template <bool INT_ACC>
+    __device__ __forceinline__ uint32_t store4(uint4 w, int64_t row, int64_t col, uint32_t vmax) const
+    {
+        const uint32_t raw[4] = {w.x, w.y, w.z, w.w};
+        const int n = p.N - col < 4 ? (int)(p.N - col) : 4;
+        const int64_t o = row * p.ldo + col;
+        if (p.out_dt == DT_INT32) {
+            int32_t *out = static_cast<int32_t *>(p.out) + o;
+            if (n == 4 && p.out_vec4) *reinterpret_cast<uint4 *>(out) = w;
+            else for (int e = 0; e < n; ++e) out[e] = (int32_t)raw[e];
+            return vmax;
+        }
+        const float s_row = p.sa[row * p.sa_stride];
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t c = col + (e < n ? e : 0);
+            const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
+            float t = a * s_row * p.sb[c * p.sb_stride];
+            if (p.bias_dt >= 0) t += bias_at(c);
+            v[e] = t;
+            if (e < n) { const uint32_t b = absbits_f32(t); vmax = b > vmax ? b : vmax; }
+        }
+        if (p.out_dt == DT_BF16) {
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+            uint16_t *out = static_cast<uint16_t *>(p.out) + o;
+            if (n == 4 && p.out_vec4)
+                *reinterpret_cast<uint2 *>(out) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            else for (int e = 0; e < n; ++e) out[e] = h[e];
+        } else if (p.out_dt == DT_FP32) {
+            float *out = static_cast<float *>(p.out) + o;
+            if (n == 4 && p.out_vec4) *reinterpret_cast<float4 *>(out) = make_float4(v[0], v[1], v[2], v[3]);
+            else for (int e = 0; e < n; ++e) out[e] = v[e];
+        } else {
+            const uint32_t c = encode4<FMT_E4M3>(odiv(v[0]), odiv(v[1]), odiv(v[2]), odiv(v[3]));
+            uint8_t *out = static_cast<uint8_t *>(p.out) + o;
+            if (n == 4 && p.out_vec4) *reinterpret_cast<uint32_t *>(out) = c;
+            else for (int e = 0; e < n; ++e) out[e] = (uint8_t)(c >> (8 * e));
+        }
+        return vmax;
+    }
+};
+
+// Linear workgroup id -> (tile_m, tile_n): XCD-contiguous, then grouped.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+    const int per_group = GEMM_GM * tiles_n;
+    const int first_m = (t / per_group) * GEMM_GM;
+    const int gsize = tiles_m - first_m < GEMM_GM ? tiles_m - first_m : GEMM_GM;
+    const int in_group = t - (t / per_group) * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW>
+__global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
+{
+    typedef Mma<AF, BF> MMA;
+    typedef typename MMA::acc_t acc_t;
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+    constexpr int STAGE = (BM + BN) * GEMM_BK;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    __shared__ uint32_t red[GEMM_THREADS / 64];
+
+    int tm, tn;
+    tile_coords(p.tiles_m, p.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const int lr = lane & 15, g = lane >> 4;
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+    Stage<BM, A_MN> sa_stage;
+    Stage<BN, B_MN> sb_stage;
+    const int nk = (int)((p.K + GEMM_BK - 1) / GEMM_BK);
+    if (nk > 0) {
+        sa_stage.load(p.a, p.lda, m0, p.M, 0, p.K, p.a_aligned);
+        sb_stage.load(p.b, p.ldb, n0, p.N, 0, p.K, p.b_aligned);
+        sa_stage.store(lds);
+        sb_stage.store(lds + BM * GEMM_BK);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t *cur = lds + (kt & 1) * STAGE;
+        uint8_t *nxt = lds + ((kt + 1) & 1) * STAGE;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int64_t k0 = (int64_t)(kt + 1) * GEMM_BK;
+            sa_stage.load(p.a, p.lda, m0, p.M, k0, p.K, p.a_aligned);
+            sb_stage.load(p.b, p.ldb, n0, p.N, k0, p.K, p.b_aligned);
+        }
+        const uint8_t *as = cur, *bs = cur + BM * GEMM_BK;
+        v8i af[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = load_frag(as, wm0 + i * 16 + lr, g);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const v8i bf = load_frag(bs, wn0 + j * 16 + lr, g);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) MMA::run(acc[i][j], af[i], bf);
+        }
+        if (more) {
+            sa_stage.store(nxt);
+            sb_stage.store(nxt + BM * GEMM_BK);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue, one 16-row slab of the wave tile at a time: the slab's
+    // accumulators go to a per-wave LDS area (raw FP32 / INT32 bits), then
+    // each lane takes 4 consecutive columns of a row, so stores are
+    // contiguous along rows.
+    constexpr int EP_LD = WN + 4;                       // padded row, in words
+    uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 16 * EP_LD;
+    Epilogue epi(p);
+    uint32_t vmax = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ep[(g * 4 + r) * EP_LD + j * 16 + lr] = MMA::bits(acc[i][j], r);
+        __syncthreads();
+        constexpr int C4 = WN / 4;                       // 4-column groups per row
+#pragma unroll 1
+        for (int idx = lane; idx < 16 * C4; idx += 64) {
+            const int rr = idx / C4, c4 = idx - rr * C4;
+            const uint4 w = *reinterpret_cast<const uint4 *>(ep + rr * EP_LD + c4 * 4);
+            const int64_t row = m0 + wm0 + i * 16 + rr;
+            const int64_t col = n0 + wn0 + c4 * 4;
+            if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w, row, col, vmax);
+        }
+    }
+    if (p.out_amax) {
+        vmax = block_max_u32(vmax, red);
+        if (threadIdx.x == 0) {
+            uint32_t bits;
+            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
+        }
+    }
+}
+
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW>
+hipError_t launch_tile(GemmParams p, hipStream_t s)
+{
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = (int)((p.N + BN - 1) / BN);
+    if (p.tiles_m == 0 || p.tiles_n == 0) {
+        // Empty output: one workgroup whose tile lies wholly outside it
+        // (every load reads zeros, no store happens); it still publishes
+        // out_amax = 0 through the election.
+        p.tiles_m = p.tiles_n = 1;
+    }
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW>), dim3((unsigned)grid),
+                       dim3(GEMM_THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+// Tile size: 256 x 256 when that still gives at least two tiles per CU,
+// else 128 x 128.
+template <int AF, int BF, bool A_MN, bool B_MN>
+hipError_t launch_layout(const GemmParams &p, hipStream_t s)
+{
+    const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1>(p, s);
+    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2>(p, s);
+}
+
+template <int AF, int BF>
+hipError_t launch_formats(const GemmParams &p, int a_mn, int b_mn, hipStream_t s)
+{
+    if (!a_mn && !b_mn) return launch_layout<AF, BF, false, false>(p, s);
+    if (!a_mn && b_mn) return launch_layout<AF, BF, false, true>(p, s);
+    if (a_mn && !b_mn) return launch_layout<AF, BF, true, false>(p, s);
+    return launch_layout<AF, BF, true, true>(p, s);
+}
+
+}  // namespace ql

@@ -1,0 +1,306 @@
+// qlinear_api.cpp -- the C ABI declared in include/qlinear.h.
+//
+// Every entry point validates all arguments on the host first and enqueues
+// nothing when any check fails, mirroring the raise-before-launch checks of
+// AstrAI ops/fp8.py @5e76fbd (_fmt_int raises ValueError for an unknown
+// format; the cuda kernels raise TypeError for a wrong dtype; mm_fp8 raises
+// ValueError for an unknown out_dtype).  Then it picks a kernel instance by
+// format, layout and alignment and launches on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "internal.hpp"
+#include "qdev.hpp"
+#include "qlinear.h"
+
+namespace ql {
+hipError_t launch_qgemm_e4m3_e4m3(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
+hipError_t launch_qgemm_e4m3_e5m2(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
+hipError_t launch_qgemm_e5m2_e4m3(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
+hipError_t launch_qgemm_e5m2_e5m2(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
+hipError_t launch_qgemm_int8_int8(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
+
+hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s)
+{
+    if (a_fmt == FMT_INT8) return launch_qgemm_int8_int8(p, a_mn, b_mn, s);
+    if (a_fmt == FMT_E4M3) return b_fmt == FMT_E4M3 ? launch_qgemm_e4m3_e4m3(p, a_mn, b_mn, s)
+                                                    : launch_qgemm_e4m3_e5m2(p, a_mn, b_mn, s);
+    return b_fmt == FMT_E4M3 ? launch_qgemm_e5m2_e4m3(p, a_mn, b_mn, s)
+                             : launch_qgemm_e5m2_e5m2(p, a_mn, b_mn, s);
+}
+}  // namespace ql
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ql_status fail(ql_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+ql_status ok()
+{
+    g_last_error.clear();
+    return QL_OK;
+}
+
+ql_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(QL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t INT8_K_MAX = 133144;          // K * 127^2 <= 2^31 - 1
+constexpr int64_t MAX_DIM = (int64_t)1 << 40;   // keeps every byte offset far inside int64
+
+bool valid_fmt(int f) { return f == QL_FMT_E4M3 || f == QL_FMT_E5M2 || f == QL_FMT_INT8; }
+bool valid_gran(int g) { return g == QL_PER_TENSOR || g == QL_PER_ROW; }
+bool valid_layout(int l) { return l == QL_K_MAJOR || l == QL_MN_MAJOR; }
+bool valid_dtype(int d) { return d >= QL_DT_BF16 && d <= QL_DT_INT32; }
+
+float fmt_qmax(int fmt) { return fmt == QL_FMT_E4M3 ? 448.0f : fmt == QL_FMT_E5M2 ? 57344.0f : 127.0f; }
+float fmt_floor(int fmt) { return fmt == QL_FMT_INT8 ? 1e-8f : 1e-12f; }
+
+// ---------------------------------------------------------------------------
+ql_status check_quantize(const void *x, int x_dt, int64_t rows, int64_t cols, int64_t ldx, int gran,
+                         int fmt, const float *scale_in, const void *x_q, int64_t ldq,
+                         const float *scale_out, const void *ws)
+{
+    if (!valid_dtype(x_dt)) return fail(QL_ERR_VALUE, "quantize: unknown input dtype %d", x_dt);
+    if (x_dt != QL_DT_BF16 && x_dt != QL_DT_FP32)
+        return fail(QL_ERR_DTYPE, "quantize requires BF16 or FP32 input, got dtype %d", x_dt);
+    if (!valid_gran(gran)) return fail(QL_ERR_VALUE, "quantize: unknown granularity %d", gran);
+    if (!valid_fmt(fmt)) return fail(QL_ERR_VALUE, "quantize: unsupported format %d (expected 0=e4m3, 1=e5m2, 2=int8)", fmt);
+    if (rows < 0 || cols < 0) return fail(QL_ERR_VALUE, "quantize: negative size rows=%lld cols=%lld",
+                                          (long long)rows, (long long)cols);
+    if (rows > MAX_DIM || cols > MAX_DIM) return fail(QL_ERR_VALUE, "quantize: size too large");
+    if (rows > 0 && (ldx < cols || ldq < cols))
+        return fail(QL_ERR_SHAPE, "quantize: leading dimensions ldx=%lld ldq=%lld must be >= cols=%lld",
+                    (long long)ldx, (long long)ldq, (long long)cols);
+    if (rows > 0 && cols > 0 && (!x || !x_q)) return fail(QL_ERR_NULL, "quantize: x and x_q are required");
+    if (!scale_in && !scale_out) return fail(QL_ERR_NULL, "quantize: scale_out is required under current scaling");
+    if (gran == QL_PER_TENSOR && !ws) return fail(QL_ERR_NULL, "quantize: per-tensor quantize needs a workspace");
+    if (gran == QL_PER_ROW && rows > 0x7FFFFFFF)
+        return fail(QL_ERR_UNSUPPORTED, "quantize: per-row quantize supports at most 2^31-1 rows");
+    return QL_OK;
+}
+
+ql::QzParams make_qz(const void *x, int x_dt, int64_t rows, int64_t cols, int64_t ldx, int gran, int fmt,
+                     const float *scale_in, void *x_q, int64_t ldq, float *scale_out, float *amax_out,
+                     uint32_t *slot)
+{
+    ql::QzParams p{};
+    p.x = x; p.rows = rows; p.cols = cols; p.ldx = ldx;
+    p.xq = x_q; p.ldq = ldq;
+    p.scale_out = scale_out; p.amax_out = amax_out;
+    p.scale_src = scale_in ? scale_in : scale_out;
+    p.ws = slot;
+    p.qmax = fmt_qmax(fmt);
+    p.floor = fmt_floor(fmt);
+    p.n_elems = rows * cols;
+    p.per_row = gran == QL_PER_ROW;
+    p.delayed = scale_in != nullptr;
+    const bool al = aligned16(x) && aligned16(x_q);
+    const bool flat = (ldx == cols && ldq == cols) || rows <= 1;
+    const bool rowvec = cols % 16 == 0 && ldx % 16 == 0 && ldq % 16 == 0;
+    if (flat && al) {
+        p.mode = 0;
+        p.n_units = p.n_elems / 16;
+    } else if (rowvec && al) {
+        p.mode = 1;
+        p.units_per_row = cols / 16;
+        p.n_units = rows * p.units_per_row;
+    } else {
+        p.mode = 2;
+    }
+    p.vec_rows = rowvec && al;
+    if (p.per_row) p.units_per_row = cols / 16;
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+    const void *a_q; int a_fmt, a_lay; int64_t lda;
+    const void *b_q; int b_fmt, b_lay; int64_t ldb;
+    int64_t M, N, K;
+    const float *sa; int sa_gran; const float *sb; int sb_gran;
+    const void *bias; int bias_dt;
+    void *out; int out_dt; int64_t ldo;
+    const float *out_scale; float *out_amax; void *ws;
+};
+
+ql_status check_gemm(const GemmArgs &g)
+{
+    if (!valid_fmt(g.a_fmt) || !valid_fmt(g.b_fmt))
+        return fail(QL_ERR_VALUE, "qgemm: unsupported format a=%d b=%d", g.a_fmt, g.b_fmt);
+    if ((g.a_fmt == QL_FMT_INT8) != (g.b_fmt == QL_FMT_INT8))
+        return fail(QL_ERR_DTYPE, "qgemm: INT8 operands pair only with INT8 (got a=%d b=%d)", g.a_fmt, g.b_fmt);
+    if (!valid_layout(g.a_lay) || !valid_layout(g.b_lay))
+        return fail(QL_ERR_VALUE, "qgemm: unknown layout a=%d b=%d", g.a_lay, g.b_lay);
+    if (!valid_gran(g.sa_gran) || !valid_gran(g.sb_gran))
+        return fail(QL_ERR_VALUE, "qgemm: unknown scale granularity sa=%d sb=%d", g.sa_gran, g.sb_gran);
+    if (!valid_dtype(g.out_dt)) return fail(QL_ERR_VALUE, "qgemm: unknown output dtype %d", g.out_dt);
+    if (g.out_dt == QL_DT_INT32 && g.a_fmt != QL_FMT_INT8)
+        return fail(QL_ERR_DTYPE, "qgemm: INT32 output needs INT8 operands");
+    if (g.M < 0 || g.N < 0 || g.K < 0)
+        return fail(QL_ERR_VALUE, "qgemm: negative size M=%lld N=%lld K=%lld", (long long)g.M, (long long)g.N, (long long)g.K);
+    if (g.M > MAX_DIM || g.N > MAX_DIM || g.K > MAX_DIM) return fail(QL_ERR_VALUE, "qgemm: size too large");
+    if (g.a_fmt == QL_FMT_INT8 && g.K > INT8_K_MAX)
+        return fail(QL_ERR_VALUE, "qgemm: INT8 K=%lld exceeds %lld (INT32 accumulator contract)", (long long)g.K, (long long)INT8_K_MAX);
+    const int64_t a_rows = g.a_lay == QL_K_MAJOR ? g.M : g.K, a_cols = g.a_lay == QL_K_MAJOR ? g.K : g.M;
+    const int64_t b_rows = g.b_lay == QL_K_MAJOR ? g.N : g.K, b_cols = g.b_lay == QL_K_MAJOR ? g.K : g.N;
+    if (a_rows > 0 && g.lda < a_cols)
+        return fail(QL_ERR_SHAPE, "qgemm: lda=%lld smaller than the stored row (%lld)", (long long)g.lda, (long long)a_cols);
+    if (b_rows > 0 && g.ldb < b_cols)
+        return fail(QL_ERR_SHAPE, "qgemm: ldb=%lld smaller than the stored row (%lld)", (long long)g.ldb, (long long)b_cols);
+    if (g.M > 0 && g.ldo < g.N)
+        return fail(QL_ERR_SHAPE, "qgemm: ldo=%lld smaller than N=%lld", (long long)g.ldo, (long long)g.N);
+    if (g.M * g.K > 0 && !g.a_q) return fail(QL_ERR_NULL, "qgemm: a_q is required");
+    if (g.N * g.K > 0 && !g.b_q) return fail(QL_ERR_NULL, "qgemm: b_q is required");
+    if (g.M * g.N > 0 && !g.out) return fail(QL_ERR_NULL, "qgemm: out is required");
+    if (g.out_dt != QL_DT_INT32 && (!g.sa || !g.sb)) return fail(QL_ERR_NULL, "qgemm: sa and sb are required");
+    if (g.bias && g.out_dt != QL_DT_INT32 && g.bias_dt != QL_DT_BF16 && g.bias_dt != QL_DT_FP32)
+        return fail(QL_ERR_DTYPE, "qgemm: bias must be BF16 or FP32, got dtype %d", g.bias_dt);
+    if (g.out_dt == QL_DT_E4M3 && !g.out_scale)
+        return fail(QL_ERR_NULL, "qgemm: E4M3 output requires out_scale (the output quantization step)");
+    if (g.out_amax && !g.ws) return fail(QL_ERR_NULL, "qgemm: out_amax needs a workspace");
+    const int64_t bm = 128;
+    if (((g.M + bm - 1) / bm) * ((g.N + bm - 1) / bm) > 0x7FFFFFFF)
+        return fail(QL_ERR_UNSUPPORTED, "qgemm: output too large for one launch");
+    return QL_OK;
+}
+
+int out_elem_bytes(int dt) { return dt == QL_DT_BF16 ? 2 : dt == QL_DT_E4M3 ? 1 : 4; }
+
+ql::GemmParams make_gemm(const GemmArgs &g, uint32_t *slot)
+{
+    ql::GemmParams p{};
+    p.a = static_cast<const uint8_t *>(g.a_q);
+    p.b = static_cast<const uint8_t *>(g.b_q);
+    p.lda = g.lda; p.ldb = g.ldb;
+    p.M = g.M; p.N = g.N; p.K = g.K;
+    p.sa = g.sa; p.sb = g.sb;
+    p.sa_stride = g.sa_gran == QL_PER_ROW ? 1 : 0;
+    p.sb_stride = g.sb_gran == QL_PER_ROW ? 1 : 0;
+    p.bias = g.out_dt == QL_DT_INT32 ? nullptr : g.bias;
+    p.bias_dt = p.bias ? g.bias_dt : -1;
+    p.out = g.out; p.ldo = g.ldo; p.out_dt = g.out_dt;
+    p.out_scale = g.out_scale;
+    p.out_amax = g.out_amax;
+    p.ws = slot;
+    p.a_aligned = aligned16(g.a_q) && g.lda % 16 == 0;
+    p.b_aligned = aligned16(g.b_q) && g.ldb % 16 == 0;
+    const int eb = out_elem_bytes(g.out_dt);
+    p.out_vec4 = (reinterpret_cast<uintptr_t>(g.out) % (uintptr_t)(4 * eb)) == 0 && g.ldo % 4 == 0;
+    return p;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+size_t ql_workspace_bytes(void) { return (size_t)ql::WS_BYTES; }
+
+ql_status ql_workspace_init(void *ws, size_t bytes, void *stream)
+{
+    if (!ws) return fail(QL_ERR_NULL, "workspace_init: ws is NULL");
+    if (bytes < (size_t)ql::WS_BYTES)
+        return fail(QL_ERR_VALUE, "workspace_init: %zu bytes given, %lld needed", bytes, (long long)ql::WS_BYTES);
+    return hip_status(ql::launch_ws_zero(ws, ql::WS_BYTES, static_cast<hipStream_t>(stream)), "workspace_init");
+}
+
+ql_status ql_quantize(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
+                      ql_gran gran, ql_qfmt fmt, const float *scale_in,
+                      void *x_q, int64_t ldq, float *scale_out, float *amax_out,
+                      void *ws, void *stream)
+{
+    ql_status st = check_quantize(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, ws);
+    if (st != QL_OK) return st;
+    uint32_t *slot = ws ? ql::ws_slot(ws, ql::WS_SLOT_QA) : nullptr;
+    ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, amax_out, slot);
+    return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+ql_status ql_qgemm(const void *a_q, ql_qfmt a_fmt, ql_layout a_lay, int64_t lda,
+                   const void *b_q, ql_qfmt b_fmt, ql_layout b_lay, int64_t ldb,
+                   int64_t M, int64_t N, int64_t K,
+                   const float *sa, ql_gran sa_gran, const float *sb, ql_gran sb_gran,
+                   const void *bias, ql_dtype bias_dt,
+                   void *out, ql_dtype out_dt, int64_t ldo,
+                   const float *out_scale, float *out_amax,
+                   void *ws, void *stream)
+{
+    GemmArgs g{a_q, a_fmt, a_lay, lda, b_q, b_fmt, b_lay, ldb, M, N, K, sa, sa_gran, sb, sb_gran,
+               bias, bias_dt, out, out_dt, ldo, out_scale, out_amax, ws};
+    ql_status st = check_gemm(g);
+    if (st != QL_OK) return st;
+    uint32_t *slot = ws ? ql::ws_slot(ws, ql::WS_SLOT_GEMM) : nullptr;
+    ql::GemmParams p = make_gemm(g, slot);
+    return hip_status(ql::launch_qgemm(p, a_fmt, b_fmt, a_lay == QL_MN_MAJOR, b_lay == QL_MN_MAJOR,
+                                       static_cast<hipStream_t>(stream)), "qgemm launch");
+}
+
+ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
+                            const void *w, int64_t N,
+                            const void *bias, ql_dtype bias_dt, ql_qfmt fmt,
+                            const float *sx_in, const float *sw_in,
+                            void *out, ql_dtype out_dt, const float *out_scale, float *out_amax,
+                            void *x_q, float *sx, float *amax_x,
+                            void *w_q, float *sw, float *amax_w,
+                            void *ws, void *stream)
+{
+    if (!ws) return fail(QL_ERR_NULL, "linear_forward: a workspace is required");
+    if (!sx || !sw || !amax_x || !amax_w)
+        return fail(QL_ERR_NULL, "linear_forward: sx, sw, amax_x and amax_w are required outputs");
+    ql_status st = check_quantize(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, ws);
+    if (st != QL_OK) return st;
+    st = check_quantize(w, x_dt, N, K, K, QL_PER_TENSOR, fmt, sw_in, w_q, K, sw, ws);
+    if (st != QL_OK) return st;
+    GemmArgs g{x_q, fmt, QL_K_MAJOR, K, w_q, fmt, QL_K_MAJOR, K, M, N, K,
+               sx_in ? sx_in : sx, QL_PER_TENSOR, sw_in ? sw_in : sw, QL_PER_TENSOR,
+               bias, bias_dt, out, out_dt, N, out_scale, out_amax, ws};
+    st = check_gemm(g);
+    if (st != QL_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ql::QzParams px = make_qz(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, amax_x,
+                              ql::ws_slot(ws, ql::WS_SLOT_QA));
+    ql::QzParams pw = make_qz(w, x_dt, N, K, K, QL_PER_TENSOR, fmt, sw_in, w_q, K, sw, amax_w,
+                              ql::ws_slot(ws, ql::WS_SLOT_QB));
+    hipError_t e = ql::launch_quantize(px, x_dt, fmt, s);
+    if (e != hipSuccess) return hip_status(e, "linear_forward: quantize x");
+    e = ql::launch_quantize(pw, x_dt, fmt, s);
+    if (e != hipSuccess) return hip_status(e, "linear_forward: quantize w");
+    ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
+    return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
+}
+
+const char *ql_status_string(ql_status s)
+{
+    switch (s) {
+    case QL_OK: return "ok";
+    case QL_ERR_VALUE: return "invalid value";
+    case QL_ERR_DTYPE: return "unsupported dtype or format combination";
+    case QL_ERR_SHAPE: return "invalid shape or leading dimension";
+    case QL_ERR_NULL: return "required pointer is NULL";
+    case QL_ERR_UNSUPPORTED: return "unsupported";
+    case QL_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *ql_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,353 @@
+// quantize.hip -- absmax quantize kernels for gfx950:
+//   x_q = sat(RNE(x / scale)),  scale = max(max|x|, floor) / qmax
+// per tensor or per row, BF16/FP32 in, E4M3 / E5M2 / INT8 codes out.
+//
+// Definitions: AstrAI ops/fp8.py @5e76fbd (quantize_bf16 docstring: cast
+// with fused amax, amax returned fresh; _fp8_quantize_cpu: x.float()/scale,
+// amax clamped at 1e-12) and POPCORNBENCH "Kimi-K2.6 l2_p13" (reference
+// model steps 2-4: amax clamp 1e-8, scale = amax/127, clamp +-127, ties to
+// even).  The commit message on the AstrAI page motivates the last-workgroup
+// epilogue: the step is published on device by the final workgroup of the
+// reduction, with no extra launch and no host synchronization.
+//
+// Kernels
+//   qz_amax   per-tensor current scaling, pass 1: HBM-streaming max|x| with
+//             16-byte loads; the last workgroup publishes amax and the step.
+//   qz_cast   pass 2 (or the only pass under delayed scaling, where it also
+//             measures amax and publishes it from its last workgroup).
+//   qz_rows   per-row: one workgroup per row; the row's second read hits
+//             the cache, so HBM sees each element once.
+#include "qdev.hpp"
+#include "internal.hpp"
+
+namespace ql {
+
+constexpr int QZ_THREADS = 256;
+constexpr int QZ_UNIT = 16;            // elements per vector unit
+constexpr int QZ_MAX_BLOCKS = 2048;    // 8 workgroups of 4 waves per CU
+constexpr int QZ_UNROLL = 4;
+
+enum : int { MODE_FLAT = 0, MODE_ROWS = 1, MODE_SCALAR = 2 };
+
+// 16 consecutive input elements loaded with 16-byte loads.
+template <typename T> struct Vec16;
+
+template <> struct Vec16<uint16_t> {
+    uint32_t w[8];
+    __device__ __forceinline__ void load(const uint16_t *p)
+    {
+        const uint4 *q = reinterpret_cast<const uint4 *>(p);
+        uint4 a = q[0], b = q[1];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+    __device__ __forceinline__ float f(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+    __device__ __forceinline__ uint32_t amax_bits() const
+    {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { uint32_t t = absbits_bf16_pair(w[i]); m = t > m ? t : m; }
+        return m;
+    }
+};
+
+template <> struct Vec16<float> {
+    float v[16];
+    __device__ __forceinline__ void load(const float *p)
+    {
+        const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 a = q[i];
+            v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+        }
+    }
+    __device__ __forceinline__ float f(int i) const { return v[i]; }
+    __device__ __forceinline__ uint32_t amax_bits() const
+    {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { uint32_t t = absbits_f32(v[i]); m = t > m ? t : m; }
+        return m;
+    }
+};
+
+template <typename T> __device__ __forceinline__ float load1(const T *x, int64_t i);
+template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t *x, int64_t i) { return __uint_as_float((uint32_t)x[i] << 16); }
+template <> __device__ __forceinline__ float load1<float>(const float *x, int64_t i) { return x[i]; }
+
+template <int FMT, typename T>
+__device__ __forceinline__ uint4 encode16(const Vec16<T> &u, const Divider &div)
+{
+    uint4 o;
+    o.x = encode4<FMT>(div(u.f(0)), div(u.f(1)), div(u.f(2)), div(u.f(3)));
+    o.y = encode4<FMT>(div(u.f(4)), div(u.f(5)), div(u.f(6)), div(u.f(7)));
+    o.z = encode4<FMT>(div(u.f(8)), div(u.f(9)), div(u.f(10)), div(u.f(11)));
+    o.w = encode4<FMT>(div(u.f(12)), div(u.f(13)), div(u.f(14)), div(u.f(15)));
+    return o;
+}
+
+// Offsets of vector unit u in x and x_q for the two vector modes.
+template <int MODE>
+__device__ __forceinline__ void unit_offsets(const QzParams &p, int64_t u, int64_t &ox, int64_t &oq)
+{
+    if (MODE == MODE_FLAT) {
+        ox = oq = u * QZ_UNIT;
+    } else {
+        int64_t row = u / p.units_per_row;
+        int64_t c = (u - row * p.units_per_row) * QZ_UNIT;
+        ox = row * p.ldx + c;
+        oq = row * p.ldq + c;
+    }
+}
+
+__device__ __forceinline__ void elem_offsets(const QzParams &p, int64_t e, int64_t &ox, int64_t &oq)
+{
+    int64_t row = e / p.cols, c = e - row * p.cols;
+    ox = row * p.ldx + c;
+    oq = row * p.ldq + c;
+}
+
+// Publish amax (floored) and fl32(amax/qmax).  NaN stays NaN.
+__device__ __forceinline__ void publish(const QzParams &p, uint32_t bits, int64_t i)
+{
+    float a = __uint_as_float(bits);
+    float amax = a < p.floor ? p.floor : a;
+    if (p.amax_out) p.amax_out[i] = amax;
+    if (p.scale_out) p.scale_out[i] = amax / p.qmax;      // IEEE division
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1 of per-tensor current scaling.
+template <typename T, int MODE>
+__global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzParams p)
+{
+    const T *x = static_cast<const T *>(p.x);
+    const int64_t gtid = (int64_t)blockIdx.x * QZ_THREADS + threadIdx.x;
+    const int64_t gstride = (int64_t)gridDim.x * QZ_THREADS;
+    uint32_t m = 0;
+    if (MODE == MODE_SCALAR) {
+        for (int64_t e = gtid; e < p.n_elems; e += gstride) {
+            int64_t ox, oq;
+            elem_offsets(p, e, ox, oq);
+            uint32_t t = absbits_f32(load1<T>(x, ox));
+            m = t > m ? t : m;
+        }
+    } else {
+        int64_t u = gtid;
+        for (; u + (QZ_UNROLL - 1) * gstride < p.n_units; u += QZ_UNROLL * gstride) {
+            Vec16<T> v[QZ_UNROLL];
+#pragma unroll
+            for (int j = 0; j < QZ_UNROLL; ++j) {
+                int64_t ox, oq;
+                unit_offsets<MODE>(p, u + j * gstride, ox, oq);
+                v[j].load(x + ox);
+            }
+#pragma unroll
+            for (int j = 0; j < QZ_UNROLL; ++j) { uint32_t t = v[j].amax_bits(); m = t > m ? t : m; }
+        }
+        for (; u < p.n_units; u += gstride) {
+            int64_t ox, oq;
+            unit_offsets<MODE>(p, u, ox, oq);
+            Vec16<T> v;
+            v.load(x + ox);
+            uint32_t t = v.amax_bits();
+            m = t > m ? t : m;
+        }
+        if (MODE == MODE_FLAT)   // flat tail beyond the last whole unit
+            for (int64_t e = p.n_units * QZ_UNIT + gtid; e < p.n_elems; e += gstride) {
+                uint32_t t = absbits_f32(load1<T>(x, e));
+                m = t > m ? t : m;
+            }
+    }
+    __shared__ uint32_t red[QZ_THREADS / 64];
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) {
+        uint32_t bits;
+        if (elect_last_max(p.ws, m, &bits)) publish(p, bits, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cast with one step for the whole tensor.  MEASURE (delayed scaling): the
+// step comes from the caller and amax is measured in the same pass.
+template <typename T, int FMT, int MODE, bool MEASURE>
+__global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
+{
+    const T *x = static_cast<const T *>(p.x);
+    uint8_t *xq = static_cast<uint8_t *>(p.xq);
+    const Divider div(p.scale_src[0]);
+    const int64_t gtid = (int64_t)blockIdx.x * QZ_THREADS + threadIdx.x;
+    const int64_t gstride = (int64_t)gridDim.x * QZ_THREADS;
+    uint32_t m = 0;
+    if (MODE == MODE_SCALAR) {
+        for (int64_t e = gtid; e < p.n_elems; e += gstride) {
+            int64_t ox, oq;
+            elem_offsets(p, e, ox, oq);
+            float v = load1<T>(x, ox);
+            if (MEASURE) { uint32_t t = absbits_f32(v); m = t > m ? t : m; }
+            xq[oq] = encode1<FMT>(div(v));
+        }
+    } else {
+        int64_t u = gtid;
+        for (; u + (QZ_UNROLL - 1) * gstride < p.n_units; u += QZ_UNROLL * gstride) {
+            Vec16<T> v[QZ_UNROLL];
+            int64_t oq[QZ_UNROLL];
+#pragma unroll
+            for (int j = 0; j < QZ_UNROLL; ++j) {
+                int64_t ox;
+                unit_offsets<MODE>(p, u + j * gstride, ox, oq[j]);
+                v[j].load(x + ox);
+            }
+#pragma unroll
+            for (int j = 0; j < QZ_UNROLL; ++j) {
+                if (MEASURE) { uint32_t t = v[j].amax_bits(); m = t > m ? t : m; }
+                *reinterpret_cast<uint4 *>(xq + oq[j]) = encode16<FMT>(v[j], div);
+            }
+        }
+        for (; u < p.n_units; u += gstride) {
+            int64_t ox, oq;
+            unit_offsets<MODE>(p, u, ox, oq);
+            Vec16<T> v;
+            v.load(x + ox);
+            if (MEASURE) { uint32_t t = v.amax_bits(); m = t > m ? t : m; }
+            *reinterpret_cast<uint4 *>(xq + oq) = encode16<FMT>(v, div);
+        }
+        if (MODE == MODE_FLAT)
+            for (int64_t e = p.n_units * QZ_UNIT + gtid; e < p.n_elems; e += gstride) {
+                float v = load1<T>(x, e);
+                if (MEASURE) { uint32_t t = absbits_f32(v); m = t > m ? t : m; }
+                xq[e] = encode1<FMT>(div(v));
+            }
+    }
+    if (MEASURE) {
+        __shared__ uint32_t red[QZ_THREADS / 64];
+        m = block_max_u32(m, red);
+        if (threadIdx.x == 0) {
+            uint32_t bits;
+            if (elect_last_max(p.ws, m, &bits)) publish(p, bits, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-row: one workgroup per row.  Pass 1 reduces the row's amax, pass 2
+// re-reads the row (from cache) and casts it with the row's step (or the
+// caller's step under delayed scaling).
+template <typename T, int FMT, bool VEC, bool DELAYED>
+__global__ __launch_bounds__(QZ_THREADS) void qz_rows(QzParams p)
+{
+    const int64_t row = blockIdx.x;
+    const T *x = static_cast<const T *>(p.x) + row * p.ldx;
+    uint8_t *xq = static_cast<uint8_t *>(p.xq) + row * p.ldq;
+    uint32_t m = 0;
+    if (VEC) {
+        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_THREADS) {
+            Vec16<T> v;
+            v.load(x + u * QZ_UNIT);
+            uint32_t t = v.amax_bits();
+            m = t > m ? t : m;
+        }
+    } else {
+        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_THREADS) {
+            uint32_t t = absbits_f32(load1<T>(x, c));
+            m = t > m ? t : m;
+        }
+    }
+    __shared__ uint32_t red[QZ_THREADS / 64];
+    m = block_max_u32(m, red);
+    const float a = __uint_as_float(m);
+    const float amax = a < p.floor ? p.floor : a;
+    const float step = amax / p.qmax;                      // IEEE division
+    if (threadIdx.x == 0) {
+        if (p.amax_out) p.amax_out[row] = amax;
+        if (p.scale_out) p.scale_out[row] = step;
+    }
+    const Divider div(DELAYED ? p.scale_src[row] : step);
+    if (VEC) {
+        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_THREADS) {
+            Vec16<T> v;
+            v.load(x + u * QZ_UNIT);
+            *reinterpret_cast<uint4 *>(xq + u * QZ_UNIT) = encode16<FMT>(v, div);
+        }
+    } else {
+        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_THREADS)
+            xq[c] = encode1<FMT>(div(load1<T>(x, c)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+__global__ void ws_fill_zero(uint32_t *ws, int64_t words)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < words) ws[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+
+static int blocks_for(int64_t work)
+{
+    int64_t b = (work + QZ_THREADS - 1) / QZ_THREADS;
+    if (b < 1) b = 1;
+    if (b > QZ_MAX_BLOCKS) b = QZ_MAX_BLOCKS;
+    return (int)b;
+}
+
+template <typename T, int FMT, int MODE>
+static hipError_t launch_tensor_mode(const QzParams &p, hipStream_t s)
+{
+    const int64_t work = MODE == MODE_SCALAR ? p.n_elems : (p.n_units > 0 ? p.n_units : p.n_elems);
+    const int blocks = blocks_for(work);
+    if (p.delayed) {
+        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((qz_amax<T, MODE>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
+        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, false>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int FMT>
+static hipError_t launch_fmt(const QzParams &p, hipStream_t s)
+{
+    if (p.per_row) {
+        if (p.rows == 0) return hipSuccess;
+        const dim3 grid((unsigned)p.rows);
+        if (p.vec_rows) {
+            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, true, true>), grid, dim3(QZ_THREADS), 0, s, p);
+            else hipLaunchKernelGGL((qz_rows<T, FMT, true, false>), grid, dim3(QZ_THREADS), 0, s, p);
+        } else {
+            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, false, true>), grid, dim3(QZ_THREADS), 0, s, p);
+            else hipLaunchKernelGGL((qz_rows<T, FMT, false, false>), grid, dim3(QZ_THREADS), 0, s, p);
+        }
+        return hipGetLastError();
+    }
+    switch (p.mode) {
+    case MODE_FLAT: return launch_tensor_mode<T, FMT, MODE_FLAT>(p, s);
+    case MODE_ROWS: return launch_tensor_mode<T, FMT, MODE_ROWS>(p, s);
+    default: return launch_tensor_mode<T, FMT, MODE_SCALAR>(p, s);
+    }
+}
+
+hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s)
+{
+    if (in_dt == DT_BF16) {
+        if (fmt == FMT_E4M3) return launch_fmt<uint16_t, FMT_E4M3>(p, s);
+        if (fmt == FMT_E5M2) return launch_fmt<uint16_t, FMT_E5M2>(p, s);
+        return launch_fmt<uint16_t, FMT_INT8>(p, s);
+    }
+    if (fmt == FMT_E4M3) return launch_fmt<float, FMT_E4M3>(p, s);
+    if (fmt == FMT_E5M2) return launch_fmt<float, FMT_E5M2>(p, s);
+    return launch_fmt<float, FMT_INT8>(p, s);
+}
+
+hipError_t launch_ws_zero(void *ws, int64_t bytes, hipStream_t s)
+{
+    const int64_t words = bytes / 4;
+    const unsigned blocks = (unsigned)((words + 255) / 256);
+    hipLaunchKernelGGL(ws_fill_zero, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t *>(ws), words);
+    return hipGetLastError();
+}
+
+}  // namespace ql

@@ -36,3 +36,13 @@ def orc():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+def pytest_runtest_setup(item):
+    """GPU tests fail (never skip) on a machine without a GPU, so a silent
+    skip can never pass for a parity result."""
+    if item.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.fail("test marked gpu but no GPU is visible")
+        print(f"\n[gpu case] {item.nodeid}", flush=True)

@@ -1,0 +1,278 @@
+"""GPU parity of ql_qgemm against the oracle.
+
+INT8 accumulators are compared bit for bit.  Float outputs use the bound in
+tests/tolerance.py (1 BF16 ulp of the reference plus the matrix cores'
+truncation bound H and FP32 accumulation); inputs whose every intermediate
+is exact must match bit for bit.  E4M3 outputs must lie in the acceptance
+set of the exact value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_quantized_gemm_amd as q
+from precision_quantized_gemm_amd import synth
+from tolerance import check_float, check_fp8_out
+
+pytestmark = pytest.mark.gpu
+
+FMT = {0: "e4m3", 1: "e5m2", 2: "int8"}
+LAY = {0: "k_major", 1: "mn_major"}
+GR = {0: "per_tensor", 1: "per_row"}
+
+
+def finite_codes(orc, seed, stream, rows, cols, fmt):
+    c = synth.random_codes(seed, stream, rows, cols)
+    if fmt == 2:
+        return np.where(c == 0x80, 0, c).astype(np.uint8)
+    return np.where(np.isfinite(orc.fp8_decode_array(c, fmt)), c, c & 0x70).astype(np.uint8)
+
+
+def storage(codes_logical, lay):
+    """[MN, K] logical codes -> storage array for the layout."""
+    return np.ascontiguousarray(codes_logical if lay == 0 else codes_logical.T)
+
+
+def run_gpu(a_st, af, al, b_st, bf, bl, K, sa, sag, sb, sbg, bias=None, out_dtype="bf16",
+            out_scale=None, out_amax=False):
+    dev = "cuda"
+    t = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    res = q.qgemm(t(a_st), FMT[af], t(b_st), FMT[bf], t(np.asarray(sa, np.float32)), t(np.asarray(sb, np.float32)),
+                  a_layout=LAY[al], b_layout=LAY[bl], sa_granularity=GR[sag], sb_granularity=GR[sbg],
+                  bias=None if bias is None else t(bias), out_dtype=out_dtype,
+                  out_scale=None if out_scale is None else t(np.asarray([out_scale], np.float32)),
+                  out_amax=out_amax, K=K)
+    torch.cuda.synchronize()
+    if out_amax:
+        return res[0].cpu(), res[1].item()
+    return res.cpu()
+
+
+def out_values(out_cpu):
+    if out_cpu.dtype == torch.bfloat16:
+        return out_cpu.to(torch.float64).numpy()
+    return out_cpu.numpy().astype(np.float64) if out_cpu.dtype != torch.uint8 else out_cpu.numpy()
+
+
+def oracle_entries(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, sa, sag, sb, sbg, bias):
+    acc, S, iacc, H = orc.qgemm_entries(a_st, af, al, b_st, bf, bl, K, ms, ns)
+    v = orc.epilogue(acc, ms, ns, np.asarray(sa, np.float32), sag, np.asarray(sb, np.float32), sbg, bias)
+    sa_ = np.asarray(sa, np.float32)[ms if sag else np.zeros_like(ms)].astype(np.float64)
+    sb_ = np.asarray(sb, np.float32)[ns if sbg else np.zeros_like(ns)].astype(np.float64)
+    return acc, S, iacc, H, v, sa_ * sb_
+
+
+def all_entries(M, N):
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    return mm.ravel().astype(np.int64), nn.ravel().astype(np.int64)
+
+
+def sampled_entries(M, N, rows=4, cols=4, rand=2048, seed=0):
+    """`rows` full output rows, `cols` full output columns and `rand` random
+    entries, as (ms, ns) index arrays."""
+    rng = np.random.default_rng(seed)
+    r = rng.choice(M, min(rows, M), replace=False)
+    c = rng.choice(N, min(cols, N), replace=False)
+    ms = [np.repeat(r, N), np.tile(np.arange(M), len(c)), rng.integers(0, M, rand)]
+    ns = [np.tile(np.arange(N), len(r)), np.repeat(c, M), rng.integers(0, N, rand)]
+    return np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+
+
+def bias_of(bias, ns):
+    return None if bias is None else np.asarray(bias, np.float64)[ns]
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (1, 1), (2, 2)])
+@pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_exact_special_case(orc, af, bf, al, bl):
+    """Integer inputs |v| <= 8, power-of-two scales and small K keep every
+    intermediate exact, so BF16 / FP32 outputs match bit for bit."""
+    M, N, K = 150, 70, 200
+    rng = np.random.default_rng(af * 10 + bf + 100 * al + 1000 * bl)
+    ints = lambda r, c: rng.integers(-8, 9, (r, c))
+    enc = (lambda v, f: np.vectorize(lambda x: orc.fp8_encode(float(x), f))(v).astype(np.uint8)) if af != 2 else None
+    A, B = ints(M, K), ints(N, K)
+    if af == 2:
+        a = A.astype(np.int8).view(np.uint8)
+        b = B.astype(np.int8).view(np.uint8)
+    else:
+        a, b = enc(A, af), enc(B, bf)
+    ref = (A @ B.T).astype(np.float64) * 0.25 * 2.0
+    for odt in ("bf16", "fp32"):
+        out = run_gpu(storage(a, al), af, al, storage(b, bl), bf, bl, K, [0.25], 0, [2.0], 0, out_dtype=odt)
+        got = out_values(out)
+        exp = ref if odt == "fp32" else torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(got, exp), (odt, np.argwhere(got != exp)[:5])
+
+
+def test_int8_rowwise_workload(orc):
+    """Per-row INT8 (scmp_kernels quickstart shapes): INT32 accumulator bit
+    exact over the whole output, FP32 output acc*sa[m]*sb[n] within 3 FP32
+    roundings."""
+    d = synth.workload("rowwise_int8")
+    qa, sa, _ = orc.quantize(d["a"].numpy(), 1, 2)
+    qb, sb, _ = orc.quantize(d["b"].numpy(), 1, 2)
+    M, K = qa.shape
+    N = qb.shape[0]
+    ms, ns = all_entries(M, N)
+    acc, S, iacc, H, v, sasb = oracle_entries(orc, qa, 2, 0, qb, 2, 0, K, ms, ns, sa, 1, sb, 1, None)
+    out_i = run_gpu(qa, 2, 0, qb, 2, 0, K, sa, 1, sb, 1, out_dtype="int32").numpy().ravel()
+    assert np.array_equal(out_i.astype(np.int64), iacc)
+    out_f = out_values(run_gpu(qa, 2, 0, qb, 2, 0, K, sa, 1, sb, 1, out_dtype="fp32")).ravel()
+    assert np.all(np.abs(out_f - v) <= 3 * 2.0 ** -24 * np.abs(v) + 1e-45)
+
+
+def _fp8_case(orc, a_log, af, al, b_log, bf, bl, K, sa, sb, bias, out_dtype, entries, what,
+              out_scale=None):
+    a_st, b_st = storage(a_log, al), storage(b_log, bl)
+    M, N = a_log.shape[0], b_log.shape[0]
+    ms, ns = entries if entries is not None else all_entries(M, N)
+    acc, S, iacc, H, v, sasb = oracle_entries(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, sa, 0, sb, 0, bias)
+    out = run_gpu(a_st, af, al, b_st, bf, bl, K, sa, 0, sb, 0, bias=bias, out_dtype=out_dtype,
+                  out_scale=out_scale)
+    got = out_values(out)[ms, ns]
+    if out_dtype == "e4m3":
+        return dict(differ=check_fp8_out(got, v, S, H, sasb, K, out_scale, orc, bias=bias_of(bias, ns), what=what))
+    return check_float(got, v, S, H, sasb, K, bias=bias_of(bias, ns), what=what)
+
+
+def test_tiny_linear_gemm(orc):
+    d = synth.workload("tiny_linear")
+    xq, sx, _ = orc.quantize(synth.bf16_bits(d["x"]), 0, 0)
+    wq, sw, _ = orc.quantize(synth.bf16_bits(d["w"]), 0, 0)
+    rep = _fp8_case(orc, xq, 0, 0, wq, 0, 0, 128, sx, sw, d["bias"].numpy(), "bf16", None, "tiny_linear")
+    print("tiny_linear", rep)
+
+
+def test_mlp_up_gemm(orc):
+    d = synth.workload("mlp_up")
+    xq, sx, _ = orc.quantize(synth.bf16_bits(d["x"]), 0, 0)
+    wq, sw, _ = orc.quantize(synth.bf16_bits(d["w"]), 0, 0)
+    ent = sampled_entries(2048, 4096, seed=3)
+    rep = _fp8_case(orc, xq, 0, 0, wq, 0, 0, 1024, sx, sw, d["bias"].numpy(), "bf16", ent, "mlp_up")
+    print("mlp_up", rep)
+
+
+def test_mlp_backward_gemms(orc):
+    """dX = G @ W (B MN-major) and dW = G^T @ X (A and B MN-major), with E5M2
+    gradient codes and E4M3 weight / activation codes."""
+    d = synth.workload("mlp_backward")
+    gq, sg, _ = orc.quantize(synth.bf16_bits(d["g"]), 0, 1)       # [2048, 4096] E5M2
+    xq, sx, _ = orc.quantize(synth.bf16_bits(d["x"]), 0, 0)       # [2048, 1024]
+    wq, sw, _ = orc.quantize(synth.bf16_bits(d["w"]), 0, 0)       # [4096, 1024]
+    # dX[t, i] = sum_o G[t, o] W[o, i]: A = G (K-major), B[n=i, k=o] = W[o, i] -> storage W is MN-major
+    ent = sampled_entries(2048, 1024, seed=4)
+    a_st, b_st = gq, wq
+    acc, S, _, H, v, sasb = oracle_entries(orc, a_st, 1, 0, b_st, 0, 1, 4096, ent[0], ent[1], sg, 0, sw, 0, None)
+    got = out_values(run_gpu(a_st, 1, 0, b_st, 0, 1, 4096, sg, 0, sw, 0))[ent]
+    print("dX", check_float(got, v, S, H, sasb, 4096, what="dX"))
+    # dW[o, i] = sum_t G[t, o] X[t, i]: A[m=o, k=t] = G[t, o] (MN-major), B[n=i, k=t] = X[t, i] (MN-major)
+    ent = sampled_entries(4096, 1024, seed=5)
+    acc, S, _, H, v, sasb = oracle_entries(orc, gq, 1, 1, xq, 0, 1, 2048, ent[0], ent[1], sg, 0, sx, 0, None)
+    got = out_values(run_gpu(gq, 1, 1, xq, 0, 1, 2048, sg, 0, sx, 0))[ent]
+    print("dW", check_float(got, v, S, H, sasb, 2048, what="dW"))
+
+
+@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("shape", [(300, 200, 1000), (33, 17, 5), (1, 1, 1), (129, 257, 130)])
+def test_ragged_all_layouts(orc, af, bf, al, bl, shape):
+    """M, N, K off every tile multiple (K tails that split a 16-byte chunk),
+    all four layout combinations, random finite codes of both formats."""
+    M, N, K = shape
+    a = finite_codes(orc, 11, af * 4 + al, M, K, af)
+    b = finite_codes(orc, 12, bf * 4 + bl, N, K, bf)
+    bias = synth.normal(13, 0, N, 0.5)
+    rep = _fp8_case(orc, a, af, al, b, bf, bl, K, [0.003], [1.5], bias, "fp32", None,
+                    f"ragged {shape} fmt={af},{bf} lay={al},{bl}")
+    assert rep["n"] == M * N
+
+
+@pytest.mark.parametrize("al,bl", [(0, 0), (1, 1)])
+def test_int8_ragged_per_row(orc, al, bl):
+    M, N, K = 131, 67, 333
+    a = finite_codes(orc, 21, al, M, K, 2)
+    b = finite_codes(orc, 22, bl, N, K, 2)
+    sa = synth.normal(23, 0, M, 0.1).astype(np.float32) ** 2 + 1e-3
+    sb = synth.normal(23, 1, N, 0.1).astype(np.float32) ** 2 + 1e-3
+    ms, ns = all_entries(M, N)
+    acc, S, iacc, H, v, sasb = oracle_entries(orc, storage(a, al), 2, al, storage(b, bl), 2, bl, K, ms, ns, sa, 1, sb, 1, None)
+    out_i = run_gpu(storage(a, al), 2, al, storage(b, bl), 2, bl, K, sa, 1, sb, 1, out_dtype="int32").numpy().ravel()
+    assert np.array_equal(out_i.astype(np.int64), iacc)
+    out_b = out_values(run_gpu(storage(a, al), 2, al, storage(b, bl), 2, bl, K, sa, 1, sb, 1, out_dtype="bf16")).ravel()
+    check_float(out_b, v, S, H, sasb, K, fp8=False, what="int8 bf16 out")
+
+
+def test_unaligned_leading_dims(orc):
+    """Leading dimensions that are not multiples of 16 force the byte-wise
+    load path; results must not change."""
+    M, N, K = 70, 90, 300
+    a = finite_codes(orc, 31, 0, M, K, 0)
+    b = finite_codes(orc, 31, 1, N, K, 0)
+    lda, ldb = K + 7, K + 3
+    a_w = np.zeros((M, lda), np.uint8); a_w[:, :K] = a
+    b_w = np.zeros((N, ldb), np.uint8); b_w[:, :K] = b
+    ta = torch.from_numpy(a_w).cuda()[:, :K]
+    tb = torch.from_numpy(b_w).cuda()[:, :K]
+    sa = torch.tensor([0.01], device="cuda")
+    sb = torch.tensor([0.02], device="cuda")
+    out = q.qgemm(ta, "e4m3", tb, "e4m3", sa, sb, out_dtype="fp32")
+    ref = q.qgemm(torch.from_numpy(a).cuda(), "e4m3", torch.from_numpy(b).cuda(), "e4m3", sa, sb, out_dtype="fp32")
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    ms, ns = all_entries(M, N)
+    acc, S, _, H, v, sasb = oracle_entries(orc, a, 0, 0, b, 0, 0, K, ms, ns, [0.01], 0, [0.02], 0, None)
+    check_float(out.cpu().numpy().ravel(), v, S, H, sasb, K, what="unaligned ld")
+
+
+def test_degenerate_sizes(orc):
+    """K = 0 gives bias only; M = 0 / N = 0 write nothing; out_amax of an
+    empty output is 0."""
+    dev = "cuda"
+    bias = torch.tensor([1.5, -2.0, 0.25], device=dev)
+    a = torch.zeros((4, 0), dtype=torch.uint8, device=dev)
+    b = torch.zeros((3, 0), dtype=torch.uint8, device=dev)
+    s = torch.ones(1, device=dev)
+    out, amax = q.qgemm(a, "e4m3", b, "e4m3", s, s, bias=bias, out_dtype="fp32", out_amax=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), bias.cpu().expand(4, 3)) and amax == 2.0
+    a = torch.zeros((0, 64), dtype=torch.uint8, device=dev)
+    b = torch.zeros((5, 64), dtype=torch.uint8, device=dev)
+    out, amax = q.qgemm(a, "e4m3", b, "e4m3", s, s, out_dtype="bf16", out_amax=True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 5) and amax == 0.0
+
+
+def test_out_amax_and_fp8_output(orc):
+    """FP32 output's own max|v| equals out_amax exactly; E4M3 output codes
+    are in the acceptance set of the exact values."""
+    M, N, K = 520, 300, 700
+    a = finite_codes(orc, 41, 0, M, K, 0)
+    b = finite_codes(orc, 41, 1, N, K, 0)
+    bias = synth.normal(42, 0, N, 1.0)
+    out, amax = run_gpu(a, 0, 0, b, 0, 0, K, [0.002], 0, [0.003], 0, bias=bias, out_dtype="fp32", out_amax=True)
+    assert amax == np.abs(out.numpy()).max()
+    os_ = np.float32(amax / 448.0 * 0.5)      # half the step: about 1/8 of the outputs saturate
+    rep = _fp8_case(orc, a, 0, 0, b, 0, 0, K, [0.002], [0.003], bias, "e4m3", None, "fp8 out", out_scale=os_)
+    print("fp8 out", rep)
+
+
+def test_large_fp8_sampled(orc):
+    """The large FP8 workload at full size (16384 x 8192 x 8192, E4M3 output
+    with out_scale = amax_prev/448) on sampled outputs: 4 full rows, 4 full
+    columns, 4096 random entries.  amax_prev is the oracle's max |v| over the
+    sampled rows (a previous measurement of the same product)."""
+    d = synth.workload("large_fp8")
+    aq, sa, _ = orc.quantize(synth.bf16_bits(d["a"]), 0, 0)
+    bq, sb, _ = orc.quantize(synth.bf16_bits(d["b"]), 0, 0)
+    M, K = aq.shape
+    N = bq.shape[0]
+    ms, ns = sampled_entries(M, N, rows=4, cols=4, rand=4096, seed=6)
+    acc, S, _, H, v, sasb = oracle_entries(orc, aq, 0, 0, bq, 0, 0, K, ms, ns, sa, 0, sb, 0, None)
+    amax_prev = np.abs(v[: 4 * N]).max()
+    os_ = np.float32(amax_prev / 448.0)
+    out = run_gpu(aq, 0, 0, bq, 0, 0, K, sa, 0, sb, 0, out_dtype="e4m3", out_scale=os_)
+    got = out.numpy()[ms, ns]
+    differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, what="large_fp8")
+    print("large_fp8 differing codes:", differ, "of", got.size)
