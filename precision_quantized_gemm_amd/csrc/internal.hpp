@@ -57,6 +57,7 @@ struct GemmParams {
     uint32_t *ws;                   // workspace slot for out_amax
     int a_aligned, b_aligned;       // 16-byte loads allowed
     int out_vec4;                   // 4 consecutive outputs may be stored as one vector
+    int fast;                       // branch-free buffer-load staging applies
     int tiles_m, tiles_n;
 };
 

@@ -49,12 +49,16 @@ __device__ __forceinline__ uint32_t absbits_f32(float x) { return __float_as_uin
 // quotient large enough to matter for any code (>= 2^-17) implies
 // |x| >= 2^-81.  Quotients far beyond every format's range (|q0| >= 2^120,
 // including an overflow to inf) skip the correction; they saturate anyway.
+// A zero q0 is returned as is: the correction would turn -0 into +0
+// (-0 + +0 = +0 under round-to-nearest), and the sign of a zero quotient is
+// part of the FP8 code.
 __device__ __forceinline__ float qdiv_fast(float x, float s, float inv)
 {
     float q0 = x * inv;
     float r = __builtin_fmaf(-q0, s, x);
     float q = __builtin_fmaf(r, inv, q0);
-    return __builtin_fabsf(q0) < 0x1p120f ? q : q0;
+    float a = __builtin_fabsf(q0);
+    return (a < 0x1p120f && a != 0.0f) ? q : q0;
 }
 
 struct Divider {

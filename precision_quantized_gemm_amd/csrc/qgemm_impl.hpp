@@ -32,6 +32,8 @@
 #include "qdev.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace ql {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -148,6 +150,136 @@ template <int ROWS> struct Stage<ROWS, true> {
 };
 
 // ---------------------------------------------------------------------------
+// Branch-free staging through buffer loads (the fast path).
+//
+// A buffer resource covers the operand from the tile's first row (or
+// column) on, with num_records set so that rows past the matrix fall outside
+// it; the hardware returns zeros for out-of-range loads, so no bounds test
+// is needed per load.  Chunks past K (the last K step) get an offset far
+// outside the range.  Needs 16-byte aligned operands, leading dimensions and
+// K (K-major) or MN extent (MN-major) that are multiples of 16, and byte
+// offsets below 2^31 (checked on the host).
+constexpr uint32_t BUF_OOB = 0x80000000u;
+constexpr int BUF_WORD3 = 0x00020000;   // gfx9 raw-buffer descriptor word 3
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int ROWS, bool MN_MAJOR> struct FastStage;
+
+template <int ROWS> struct FastStage<ROWS, false> {
+    static constexpr int PER = ROWS * 8 / GEMM_THREADS;
+    uint4 r[PER];
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t off[PER];      // row * ld + chunk * 16, tile relative
+    int kc;                 // this thread's chunk start within a K step
+    __device__ __forceinline__ void init(const uint8_t *base, int64_t ld, int64_t row0, int64_t rows_total, int64_t K)
+    {
+        const int64_t rows_left = rows_total - row0;
+        const int64_t bytes = rows_left > 0 ? rows_left * ld : 0;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(base + row0 * ld), (short)0,
+                                                 (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), BUF_WORD3);
+        kc = ((int)threadIdx.x & 7) * 16;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = i * GEMM_THREADS + (int)threadIdx.x;
+            off[i] = (uint32_t)((c >> 3) * ld + kc);
+        }
+        (void)K;
+    }
+    __device__ __forceinline__ void load(int64_t k0, int64_t K)
+    {
+        const bool in_k = k0 + kc < K;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) r[i] = buf_load16(rsrc, in_k ? off[i] + (uint32_t)k0 : BUF_OOB);
+    }
+    __device__ __forceinline__ void store(uint8_t *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = i * GEMM_THREADS + (int)threadIdx.x;
+            *reinterpret_cast<uint4 *>(lds + lds_off(c >> 3, c & 7)) = r[i];
+        }
+    }
+};
+
+template <int ROWS> struct FastStage<ROWS, true> {
+    static constexpr int GROUPS = ROWS / 16;
+    static constexpr int UNITS = GROUPS * (GEMM_BK / 8);
+    static_assert(UNITS % GEMM_THREADS == 0 || UNITS < GEMM_THREADS, "unit split");
+    static constexpr int PER = (UNITS + GEMM_THREADS - 1) / GEMM_THREADS;
+    uint4 r[PER][8];
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t off[PER];      // (kq*8) * ld + mn, tile relative; OOB when mn is past the matrix
+    uint32_t ld32;
+    __device__ __forceinline__ void init(const uint8_t *base, int64_t ld, int64_t row0, int64_t rows_total, int64_t K)
+    {
+        const int64_t bytes = K * ld - row0;          // rows k >= K fall outside
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(base + row0), (short)0,
+                                                 (int)(bytes > 0 ? (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0), BUF_WORD3);
+        ld32 = (uint32_t)ld;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = i * GEMM_THREADS + (int)threadIdx.x;
+            const int mg = u % GROUPS, kq = u / GROUPS;
+            const bool ok = u < UNITS && row0 + mg * 16 < rows_total;
+            off[i] = ok ? (uint32_t)(kq * 8 * ld + mg * 16) : BUF_OOB;
+        }
+    }
+    __device__ __forceinline__ void load(int64_t k0, int64_t K)
+    {
+        (void)K;
+        const uint32_t kb = (uint32_t)k0 * ld32;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                r[i][j] = buf_load16(rsrc, off[i] == BUF_OOB ? BUF_OOB : off[i] + kb + (uint32_t)j * ld32);
+    }
+    __device__ __forceinline__ void store(uint8_t *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = i * GEMM_THREADS + (int)threadIdx.x;
+            if (u >= UNITS) continue;
+            const int mg = u % GROUPS, kq = u / GROUPS;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int w = e >> 2, sh = (e & 3) * 8;
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    lo |= ((word_of(r[i][j], w) >> sh) & 0xFFu) << (8 * j);
+                    hi |= ((word_of(r[i][j + 4], w) >> sh) & 0xFFu) << (8 * j);
+                }
+                *reinterpret_cast<uint2 *>(lds + lds_off(mg * 16 + e, kq >> 1) + (kq & 1) * 8) = make_uint2(lo, hi);
+            }
+        }
+    }
+};
+
+// Generic staging adapter with the same interface (odd shapes, unaligned
+// operands): bounds-checked loads with a byte-wise fallback.
+template <int ROWS, bool MN_MAJOR> struct SafeStage {
+    Stage<ROWS, MN_MAJOR> st;
+    const uint8_t *base;
+    int64_t ld, row0, rows_total;
+    bool aligned;
+    __device__ __forceinline__ void init(const uint8_t *b, int64_t l, int64_t r0, int64_t rt, int64_t K)
+    {
+        base = b; ld = l; row0 = r0; rows_total = rt;
+        (void)K;
+    }
+    __device__ __forceinline__ void load(int64_t k0, int64_t K) { st.load(base, ld, row0, rows_total, k0, K, aligned); }
+    __device__ __forceinline__ void store(uint8_t *lds) const { st.store(lds); }
+};
+
+// ---------------------------------------------------------------------------
 template <int AF, int BF> struct Mma {
     typedef v4f acc_t;
     __device__ __forceinline__ static void run(acc_t &c, const v8i &a, const v8i &b)
@@ -254,7 +386,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
     tn = in_group / gsize;
 }
 
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW>
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST>
 __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 {
     typedef Mma<AF, BF> MMA;
@@ -277,12 +409,17 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-    Stage<BM, A_MN> sa_stage;
-    Stage<BN, B_MN> sb_stage;
+    typedef typename std::conditional<FAST, FastStage<BM, A_MN>, SafeStage<BM, A_MN> >::type StageA;
+    typedef typename std::conditional<FAST, FastStage<BN, B_MN>, SafeStage<BN, B_MN> >::type StageB;
+    StageA sa_stage;
+    StageB sb_stage;
+    sa_stage.init(p.a, p.lda, m0, p.M, p.K);
+    sb_stage.init(p.b, p.ldb, n0, p.N, p.K);
+    if constexpr (!FAST) { sa_stage.aligned = p.a_aligned; sb_stage.aligned = p.b_aligned; }
     const int nk = (int)((p.K + GEMM_BK - 1) / GEMM_BK);
     if (nk > 0) {
-        sa_stage.load(p.a, p.lda, m0, p.M, 0, p.K, p.a_aligned);
-        sb_stage.load(p.b, p.ldb, n0, p.N, 0, p.K, p.b_aligned);
+        sa_stage.load(0, p.K);
+        sb_stage.load(0, p.K);
         sa_stage.store(lds);
         sb_stage.store(lds + BM * GEMM_BK);
     }
@@ -293,8 +430,8 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
         const bool more = kt + 1 < nk;
         if (more) {
             const int64_t k0 = (int64_t)(kt + 1) * GEMM_BK;
-            sa_stage.load(p.a, p.lda, m0, p.M, k0, p.K, p.a_aligned);
-            sb_stage.load(p.b, p.ldb, n0, p.N, k0, p.K, p.b_aligned);
+            sa_stage.load(k0, p.K);
+            sb_stage.load(k0, p.K);
         }
         const uint8_t *as = cur, *bs = cur + BM * GEMM_BK;
         v8i af[TM];
@@ -349,7 +486,7 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
     }
 }
 
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW>
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST>
 hipError_t launch_tile(GemmParams p, hipStream_t s)
 {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -361,19 +498,22 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
         p.tiles_m = p.tiles_n = 1;
     }
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST>), dim3((unsigned)grid),
                        dim3(GEMM_THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 // Tile size: 256 x 256 when that still gives at least two tiles per CU,
-// else 128 x 128.
+// else 128 x 128.  p.fast selects the branch-free buffer-load staging.
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)
 {
     const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1>(p, s);
-    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2>(p, s);
+    if (p.fast) {
+        if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
+        return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);
+    }
+    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false>(p, s);
 }
 
 template <int AF, int BF>

@@ -89,7 +89,8 @@ ql_status check_quantize(const void *x, int x_dt, int64_t rows, int64_t cols, in
         return fail(QL_ERR_SHAPE, "quantize: leading dimensions ldx=%lld ldq=%lld must be >= cols=%lld",
                     (long long)ldx, (long long)ldq, (long long)cols);
     if (rows > 0 && cols > 0 && (!x || !x_q)) return fail(QL_ERR_NULL, "quantize: x and x_q are required");
-    if (!scale_in && !scale_out) return fail(QL_ERR_NULL, "quantize: scale_out is required under current scaling");
+    if (!scale_in && !scale_out && (gran == QL_PER_TENSOR || rows > 0))
+        return fail(QL_ERR_NULL, "quantize: scale_out is required under current scaling");
     if (gran == QL_PER_TENSOR && !ws) return fail(QL_ERR_NULL, "quantize: per-tensor quantize needs a workspace");
     if (gran == QL_PER_ROW && rows > 0x7FFFFFFF)
         return fail(QL_ERR_UNSUPPORTED, "quantize: per-row quantize supports at most 2^31-1 rows");
@@ -201,6 +202,15 @@ ql::GemmParams make_gemm(const GemmArgs &g, uint32_t *slot)
     p.ws = slot;
     p.a_aligned = aligned16(g.a_q) && g.lda % 16 == 0;
     p.b_aligned = aligned16(g.b_q) && g.ldb % 16 == 0;
+    // Fast staging: 16-byte aligned operands whose 16-byte chunks never
+    // straddle the matrix edge, and byte offsets that fit the 31-bit buffer
+    // range.
+    const int64_t lim = (int64_t)1 << 31;
+    const bool a_ok = p.a_aligned && (g.a_lay == QL_K_MAJOR ? g.K % 16 == 0 && (g.M + 256) * g.lda < lim
+                                                           : g.M % 16 == 0 && (g.K + 256) * g.lda < lim);
+    const bool b_ok = p.b_aligned && (g.b_lay == QL_K_MAJOR ? g.K % 16 == 0 && (g.N + 256) * g.ldb < lim
+                                                           : g.N % 16 == 0 && (g.K + 256) * g.ldb < lim);
+    p.fast = a_ok && b_ok;
     const int eb = out_elem_bytes(g.out_dt);
     p.out_vec4 = (reinterpret_cast<uintptr_t>(g.out) % (uintptr_t)(4 * eb)) == 0 && g.ldo % 4 == 0;
     return p;

@@ -176,10 +176,14 @@ def test_mlp_backward_gemms(orc):
 
 @pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (1, 1)])
 @pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 0), (1, 1)])
-@pytest.mark.parametrize("shape", [(300, 200, 1000), (33, 17, 5), (1, 1, 1), (129, 257, 130)])
+@pytest.mark.parametrize("shape", [(300, 200, 1000), (33, 17, 5), (1, 1, 1), (129, 257, 130),
+                                   (272, 144, 160), (300, 200, 1024), (33, 17, 16), (528, 784, 272)])
 def test_ragged_all_layouts(orc, af, bf, al, bl, shape):
-    """M, N, K off every tile multiple (K tails that split a 16-byte chunk),
-    all four layout combinations, random finite codes of both formats."""
+    """M, N, K off every tile multiple, all four layout combinations, random
+    finite codes of both formats.  Shapes with K (and, for MN-major operands,
+    M or N) a multiple of 16 take the branch-free buffer-load path with rows
+    past the matrix and a partial last K step; the others (K tails that split
+    a 16-byte chunk) take the bounds-checked path."""
     M, N, K = shape
     a = finite_codes(orc, 11, af * 4 + al, M, K, af)
     b = finite_codes(orc, 12, bf * 4 + bl, N, K, bf)
