@@ -1,6 +1,7 @@
 // qgemm_e4m3_e5m2.hip -- instantiations of the scaled GEMM for A in FMT_E4M3 and B in
 // FMT_E5M2 (one file per format pair so the build compiles them in parallel).
 #include "qgemm_impl.hpp"
+#include "qgemm_nt.hpp"
 
 namespace ql {
 

@@ -314,11 +314,22 @@ __device__ __forceinline__ v8i load_frag(const uint8_t *lds, int row, int g)
 
 // Fused epilogue for 4 consecutive outputs of one row:
 //   v = acc * sa[row|0] * sb[col|0] (+ bias[col]), then the output cast.
+// Per-tensor scales fold into one FP32 product sa*sb (either order of the
+// two multiplies is within the float acceptance bound).  E4M3 output
+// multiplies by RN(1/out_scale): its result differs from the correctly
+// rounded quotient by at most one FP32 rounding, which the FP8 acceptance
+// set allows for.
 struct Epilogue {
     const GemmParams &p;
-    Divider odiv;
-    __device__ __forceinline__ explicit Epilogue(const GemmParams &pp)
-        : p(pp), odiv(pp.out_dt == DT_E4M3 ? pp.out_scale[0] : 1.0f) {}
+    float inv_os;       // RN(1 / out_scale) for E4M3 output
+    float s_ab;         // sa[0] * sb[0] when both are per tensor
+    bool per_tensor;
+    __device__ __forceinline__ explicit Epilogue(const GemmParams &pp) : p(pp)
+    {
+        inv_os = pp.out_dt == DT_E4M3 ? 1.0f / pp.out_scale[0] : 1.0f;
+        per_tensor = pp.sa_stride == 0 && pp.sb_stride == 0;
+        s_ab = (per_tensor && pp.out_dt != DT_INT32) ? pp.sa[0] * pp.sb[0] : 1.0f;
+    }
 
     __device__ __forceinline__ float bias_at(int64_t col) const
     {
@@ -339,17 +350,31 @@ struct Epilogue {
             else for (int e = 0; e < n; ++e) out[e] = (int32_t)raw[e];
             return vmax;
         }
-        const float s_row = p.sa[row * p.sa_stride];
         float v[4];
+        if (per_tensor) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t c = col + (e < n ? e : 0);
-            const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
-            float t = a * s_row * p.sb[c * p.sb_stride];
-            if (p.bias_dt >= 0) t += bias_at(c);
-            v[e] = t;
-            if (e < n) { const uint32_t b = absbits_f32(t); vmax = b > vmax ? b : vmax; }
+            for (int e = 0; e < 4; ++e) v[e] = (INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e])) * s_ab;
+        } else {
+            const float s_row = p.sa[row * p.sa_stride];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t c = col + (e < n ? e : 0);
+                const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
+                v[e] = a * s_row * p.sb[c * p.sb_stride];
+            }
         }
+        if (p.bias_dt >= 0) {
+            if (n == 4 && p.bias_dt == DT_FP32 && (col & 3) == 0 && p.out_vec4) {
+                const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.bias) + col);
+                v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bias_at(col + (e < n ? e : 0));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) { const uint32_t b = absbits_f32(v[e]); vmax = b > vmax ? b : vmax; }
         if (p.out_dt == DT_BF16) {
             uint16_t h[4];
 #pragma unroll
@@ -363,7 +388,7 @@ struct Epilogue {
             if (n == 4 && p.out_vec4) *reinterpret_cast<float4 *>(out) = make_float4(v[0], v[1], v[2], v[3]);
             else for (int e = 0; e < n; ++e) out[e] = v[e];
         } else {
-            const uint32_t c = encode4<FMT_E4M3>(odiv(v[0]), odiv(v[1]), odiv(v[2]), odiv(v[3]));
+            const uint32_t c = encode4<FMT_E4M3>(v[0] * inv_os, v[1] * inv_os, v[2] * inv_os, v[3] * inv_os);
             uint8_t *out = static_cast<uint8_t *>(p.out) + o;
             if (n == 4 && p.out_vec4) *reinterpret_cast<uint32_t *>(out) = c;
             else for (int e = 0; e < n; ++e) out[e] = (uint8_t)(c >> (8 * e));
@@ -505,10 +530,15 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
 
 // Tile size: 256 x 256 when that still gives at least two tiles per CU,
 // else 128 x 128.  p.fast selects the branch-free buffer-load staging.
+template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
+
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)
 {
     const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    // K-major operands with at least one 256 x 256 tile per CU: the
+    // pipelined direct-to-LDS kernel.
+    if (p.fast && !A_MN && !B_MN && big >= 256) return launch_nt<AF, BF>(p, s);
     if (p.fast) {
         if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
         return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);

@@ -1,6 +1,7 @@
 // qgemm_int8_int8.hip -- instantiations of the scaled GEMM for A in FMT_INT8 and B in
 // FMT_INT8 (one file per format pair so the build compiles them in parallel).
 #include "qgemm_impl.hpp"
+#include "qgemm_nt.hpp"
 
 namespace ql {
 

@@ -280,3 +280,30 @@ def test_large_fp8_sampled(orc):
     got = out.numpy()[ms, ns]
     differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, what="large_fp8")
     print("large_fp8 differing codes:", differ, "of", got.size)
+
+
+@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (2, 2)])
+def test_pipelined_nt_path_ragged(orc, af, bf):
+    """Shapes with at least 256 tiles of 256 x 256 take the pipelined
+    direct-to-LDS kernel: ragged M and N (partial edge tiles) and a K whose
+    last 64-byte step is partial.  Sampled entries include the last rows and
+    columns."""
+    M, N, K = 4133, 4101, 1040
+    a = finite_codes(orc, 51, af, M, K, af)
+    b = finite_codes(orc, 52, bf, N, K, bf)
+    rng = np.random.default_rng(53)
+    rows = np.array([0, 255, 256, 4095, M - 1])
+    cols = np.array([0, 255, 4096, N - 2, N - 1])
+    ms = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 2000)])
+    ns = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 2000)])
+    ms, ns = ms.astype(np.int64), ns.astype(np.int64)
+    if af == 2:
+        acc, S, iacc, H, v, sasb = oracle_entries(orc, a, 2, 0, b, 2, 0, K, ms, ns, [1.0], 0, [1.0], 0, None)
+        out = run_gpu(a, 2, 0, b, 2, 0, K, [1.0], 0, [1.0], 0, out_dtype="int32").numpy()
+        assert np.array_equal(out[ms, ns].astype(np.int64), iacc)
+        return
+    bias = synth.normal(54, 0, N, 0.5)
+    acc, S, _, H, v, sasb = oracle_entries(orc, a, af, 0, b, bf, 0, K, ms, ns, [0.004], 0, [0.5], 0, bias)
+    out = run_gpu(a, af, 0, b, bf, 0, K, [0.004], 0, [0.5], 0, bias=bias, out_dtype="bf16")
+    print("nt ragged", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, bias=bias_of(bias, ns),
+                                   what=f"nt ragged fmt={af},{bf}"))
