@@ -7,14 +7,20 @@ per-tensor E4M3 quantize of a and of b (amax reduction, on-device step,
 cast), then the scaled E4M3 GEMM 16384 x 8192 x 8192 with FP32 accumulation
 and E4M3 output (out_scale = amax_prev / 448, amax_prev being the out_amax
 of the previous step on the same inputs), which also publishes the step's
-own out_amax.  That is one ql_linear_forward call.
+own out_amax.  The step is issued as its three C-ABI calls (ql_quantize,
+ql_quantize, ql_qgemm: the same launches ql_linear_forward makes) with HIP
+events between them on the stream they run on, so every kernel's duration
+is measured inside the timed region itself.
 
 Prints one JSON line.  `value` is the step's GEMM work (2*M*N*K) divided by
-the step time (inputs resident in HBM).  `roofline` is the GEMM kernel alone
-against the dense FP8 matrix-core peak, timed with HIP events on the stream
-it is launched on; `quantize` reports the quantize kernels against HBM
-peak; `cpu_baseline` is the oracle (plain C) timed on a bounded sample of
-the same workload on this host's cores and scaled to the full step.
+the step time (inputs resident in HBM).  `roofline` is the GEMM kernel
+against the dense FP8 matrix-core peak; `quantize` reports the quantize
+calls against HBM peak; `cpu_baseline` is the oracle (plain C) timed on a
+bounded sample of the same workload on this host's cores and scaled to the
+full step.
+
+`--copy-calibration` instead times a plain 1 GiB device copy (the known-size
+kernel that scales the HBM byte counters of a profiler run) and exits.
 """
 from __future__ import annotations
 
@@ -39,7 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--kernel-reps", type=int, default=30, help="launches per per-kernel timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4, help="output rows in the oracle GEMM sample")
     return ap.parse_args()
@@ -105,6 +112,26 @@ def cpu_baseline(a_cpu, b_cpu, M, N, K, rows):
                 step_seconds_estimate=step_s)
 
 
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=10):
+    """A plain device copy of known size: every launch reads and writes
+    exactly `nbytes` of HBM, so a profiler's fetch / write byte counters on
+    it give the factor between those counters and real bytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms_per_copy": round(ms, 5),
+                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "launches": reps + 1}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -120,6 +147,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     log("generating inputs")
     d = synth.workload("large_fp8")
     a_cpu, b_cpu = d["a"], d["b"]
@@ -138,18 +168,28 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     P = lambda t: t.data_ptr()
 
-    def step():
-        q.ql_linear_forward(P(a), _lib.QL_DT_BF16, M, K, P(b), N, None, 0, _lib.QL_FMT_E4M3, None, None,
-                            P(out), _lib.QL_DT_E4M3, P(out_scale), P(out_amax), P(x_q), P(sx), P(amax_x),
-                            P(w_q), P(sw), P(amax_w), P(ws), stream)
-
-    def gemm_only():
-        q.ql_qgemm(P(x_q), 0, 0, K, P(w_q), 0, 0, K, M, N, K, P(sx), 0, P(sw), 0, None, 0,
-                   P(out), _lib.QL_DT_E4M3, N, P(out_scale), None, P(ws), stream)
-
     def quant(x, rows, xq, s, am):
         return lambda: q.ql_quantize(P(x), _lib.QL_DT_BF16, rows, K, K, 0, 0, None, P(xq), K, P(s), P(am),
                                      P(ws), stream)
+
+    qa, qb = quant(a, M, x_q, sx, amax_x), quant(b, N, w_q, sw, amax_w)
+
+    def gemm():
+        q.ql_qgemm(P(x_q), 0, 0, K, P(w_q), 0, 0, K, M, N, K, P(sx), 0, P(sw), 0, None, 0,
+                   P(out), _lib.QL_DT_E4M3, N, P(out_scale), P(out_amax), P(ws), stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        qa()
+        if ev is not None:
+            ev[1].record()
+        qb()
+        if ev is not None:
+            ev[2].record()
+        gemm()
+        if ev is not None:
+            ev[3].record()
 
     log("warmup")
     step()
@@ -159,21 +199,23 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    ms_step = time_events(step, args.steps, torch)
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
+    ms_step = events[0][0].elapsed_time(events[-1][3]) / args.steps
+    ms_qa = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
+    ms_qb = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
+    ms_gemm = sum(ev[2].elapsed_time(ev[3]) for ev in events) / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
-
-    log("per-kernel timing")
-    ms_gemm = time_events(gemm_only, args.kernel_reps, torch)
-    ms_qa = time_events(quant(a, M, x_q, sx, amax_x), args.kernel_reps, torch)
-    ms_qb = time_events(quant(b, N, w_q, sw, amax_w), args.kernel_reps, torch)
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
-    # quantize traffic: per-tensor current scaling reads x twice (amax pass,
-    # cast pass) and writes 1 byte per element: 5 B/elem of BF16 input; the
-    # compulsory traffic is 3 B/elem.
+    # Quantize bytes per BF16 element, per-tensor current scaling: the
+    # method reads x twice (amax pass, cast pass) and writes one code byte:
+    # 5 B; the compulsory traffic is 3 B.
     qa_bytes5, qa_bytes3 = 5.0 * M * K, 3.0 * M * K
     qb_bytes5 = 5.0 * N * K
     qa_gbps = qa_bytes5 / (ms_qa * 1e-3) / 1e9
@@ -200,7 +242,7 @@ def main():
         "config": {
             "workload": "large_fp8: quantize a[16384,8192] bf16 Student-t(3) and b[8192,8192] bf16 N(0,1/8192) "
                         "per-tensor E4M3, then E4M3 GEMM 16384x8192x8192 FP32-acc, E4M3 out "
-                        "(out_scale = amax_prev/448), one ql_linear_forward per step",
+                        "(out_scale = amax_prev/448); per step ql_quantize(a), ql_quantize(b), ql_qgemm",
             "M": M, "N": N, "K": K, "parallelism": "single GPU",
         },
         "roofline": {
@@ -210,11 +252,13 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": None,
-            "kernel": "qgemm_kernel<E4M3,E4M3,K-major,K-major,256x256>",
+            "kernel": "qgemm_nt_kernel<E4M3,E4M3> (256x256x128 tiles)",
             "ms_per_launch": round(ms_gemm, 5),
+            "per_launch_flops": flops,
         },
         "quantize": {
             "a_ms": round(ms_qa, 5), "b_ms": round(ms_qb, 5),
+            "bytes_per_elem": "5 (two reads of BF16 x, one code byte written)",
             "a_GBps_5B_per_elem": round(qa_gbps, 1),
             "a_GBps_3B_per_elem": round(qa_bytes3 / (ms_qa * 1e-3) / 1e9, 1),
             "b_GBps_5B_per_elem": round(qb_gbps, 1),

@@ -170,6 +170,12 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 // ordering).  It returns the final maximum and leaves the slot zeroed for the
 // next call, so no separate clearing launch is ever needed.  Only thread 0
 // of each workgroup calls this; it returns true (and *result) in the last.
+//
+// Cost: read-modify-writes on one address are serialized by the memory
+// system (about 10 ns each on MI355X), and the acquire-release increment
+// also writes back and invalidates the XCD's L2.  Grids that finish all at
+// once (the streaming quantize kernels) therefore stay at a few hundred
+// workgroups; the grid must be one-dimensional.
 __device__ __forceinline__ bool elect_last_max(uint32_t *slot, uint32_t block_max, uint32_t *result)
 {
     __hip_atomic_fetch_max(&slot[0], block_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

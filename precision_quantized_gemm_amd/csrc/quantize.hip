@@ -14,7 +14,10 @@
 //   qz_amax   per-tensor current scaling, pass 1: HBM-streaming max|x| with
 //             16-byte loads; the last workgroup publishes amax and the step.
 //   qz_cast   pass 2 (or the only pass under delayed scaling, where it also
-//             measures amax and publishes it from its last workgroup).
+//             measures amax and publishes it from its last workgroup).  As
+//             pass 2 it walks the tensor from the end backwards, so it
+//             starts on the data pass 1 read last, which the memory-side
+//             cache (256 MB) still holds.
 //   qz_rows   per-row: one workgroup per row; the row's second read hits
 //             the cache, so HBM sees each element once.
 #include "qdev.hpp"
@@ -22,9 +25,15 @@
 
 namespace ql {
 
-constexpr int QZ_THREADS = 256;
+// Whole-tensor kernels: at most one workgroup of 16 waves per CU.  That
+// streams as fast as more, smaller workgroups (four waves per SIMD with four
+// 32-byte units in flight per lane keep 32 MiB of reads outstanding) and
+// keeps the end-of-grid election to 256 atomic pairs.
+constexpr int QZ_THREADS = 1024;
+constexpr int QZ_MAX_BLOCKS = 256;
+// Per-row kernel: one workgroup of 4 waves per row.
+constexpr int QZ_ROW_THREADS = 256;
 constexpr int QZ_UNIT = 16;            // elements per vector unit
-constexpr int QZ_MAX_BLOCKS = 2048;    // 8 workgroups of 4 waves per CU
 constexpr int QZ_UNROLL = 4;
 
 enum : int { MODE_FLAT = 0, MODE_ROWS = 1, MODE_SCALAR = 2 };
@@ -189,6 +198,8 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
             xq[oq] = encode1<FMT>(div(v));
         }
     } else {
+        // Unit u of the walk is unit n_units-1-u of the tensor in pass 2.
+        auto phys = [&](int64_t u) { return MEASURE ? u : p.n_units - 1 - u; };
         int64_t u = gtid;
         for (; u + (QZ_UNROLL - 1) * gstride < p.n_units; u += QZ_UNROLL * gstride) {
             Vec16<T> v[QZ_UNROLL];
@@ -196,7 +207,7 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
 #pragma unroll
             for (int j = 0; j < QZ_UNROLL; ++j) {
                 int64_t ox;
-                unit_offsets<MODE>(p, u + j * gstride, ox, oq[j]);
+                unit_offsets<MODE>(p, phys(u + j * gstride), ox, oq[j]);
                 v[j].load(x + ox);
             }
 #pragma unroll
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
         }
         for (; u < p.n_units; u += gstride) {
             int64_t ox, oq;
-            unit_offsets<MODE>(p, u, ox, oq);
+            unit_offsets<MODE>(p, phys(u), ox, oq);
             Vec16<T> v;
             v.load(x + ox);
             if (MEASURE) { uint32_t t = v.amax_bits(); m = t > m ? t : m; }
@@ -235,26 +246,26 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
 // re-reads the row (from cache) and casts it with the row's step (or the
 // caller's step under delayed scaling).
 template <typename T, int FMT, bool VEC, bool DELAYED>
-__global__ __launch_bounds__(QZ_THREADS) void qz_rows(QzParams p)
+__global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
 {
     const int64_t row = blockIdx.x;
     const T *x = static_cast<const T *>(p.x) + row * p.ldx;
     uint8_t *xq = static_cast<uint8_t *>(p.xq) + row * p.ldq;
     uint32_t m = 0;
     if (VEC) {
-        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_THREADS) {
+        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_ROW_THREADS) {
             Vec16<T> v;
             v.load(x + u * QZ_UNIT);
             uint32_t t = v.amax_bits();
             m = t > m ? t : m;
         }
     } else {
-        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_THREADS) {
+        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_ROW_THREADS) {
             uint32_t t = absbits_f32(load1<T>(x, c));
             m = t > m ? t : m;
         }
     }
-    __shared__ uint32_t red[QZ_THREADS / 64];
+    __shared__ uint32_t red[QZ_ROW_THREADS / 64];
     m = block_max_u32(m, red);
     const float a = __uint_as_float(m);
     const float amax = a < p.floor ? p.floor : a;
@@ -265,13 +276,13 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_rows(QzParams p)
     }
     const Divider div(DELAYED ? p.scale_src[row] : step);
     if (VEC) {
-        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_THREADS) {
+        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_ROW_THREADS) {
             Vec16<T> v;
             v.load(x + u * QZ_UNIT);
             *reinterpret_cast<uint4 *>(xq + u * QZ_UNIT) = encode16<FMT>(v, div);
         }
     } else {
-        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_THREADS)
+        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_ROW_THREADS)
             xq[c] = encode1<FMT>(div(load1<T>(x, c)));
     }
 }
@@ -315,11 +326,11 @@ static hipError_t launch_fmt(const QzParams &p, hipStream_t s)
         if (p.rows == 0) return hipSuccess;
         const dim3 grid((unsigned)p.rows);
         if (p.vec_rows) {
-            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, true, true>), grid, dim3(QZ_THREADS), 0, s, p);
-            else hipLaunchKernelGGL((qz_rows<T, FMT, true, false>), grid, dim3(QZ_THREADS), 0, s, p);
+            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, true, true>), grid, dim3(QZ_ROW_THREADS), 0, s, p);
+            else hipLaunchKernelGGL((qz_rows<T, FMT, true, false>), grid, dim3(QZ_ROW_THREADS), 0, s, p);
         } else {
-            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, false, true>), grid, dim3(QZ_THREADS), 0, s, p);
-            else hipLaunchKernelGGL((qz_rows<T, FMT, false, false>), grid, dim3(QZ_THREADS), 0, s, p);
+            if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, false, true>), grid, dim3(QZ_ROW_THREADS), 0, s, p);
+            else hipLaunchKernelGGL((qz_rows<T, FMT, false, false>), grid, dim3(QZ_ROW_THREADS), 0, s, p);
         }
         return hipGetLastError();
     }
