@@ -538,7 +538,10 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
     const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     // K-major operands with at least one 256 x 256 tile per CU: the
     // pipelined direct-to-LDS kernel.
-    if (p.fast && !A_MN && !B_MN && big >= 256) return launch_nt<AF, BF>(p, s);
+    // The pipelined kernel covers FP8 only: INT8's paired 32-deep MFMAs do
+    // not fit its register budget.
+    if constexpr (AF != FMT_INT8)
+        if (p.fast && !A_MN && !B_MN && big >= 256) return launch_nt<AF, BF>(p, s);
     if (p.fast) {
         if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
         return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);

@@ -4,7 +4,7 @@
 //
 // One workgroup of 4 waves computes a 256 x 256 output tile; each wave owns
 // a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x64_f8f6f4 (FP8,
-// per-operand formats) or pairs of v_mfma_i32_32x32x32_i8 (INT8).
+// per-operand formats; INT8 takes the general kernel).
 //
 // K advances 128 bytes per step -- whole 128-byte cache lines of every row
 // -- through 2 LDS stages of 64 KiB (256 rows of A and of B, 128 bytes per
@@ -22,13 +22,15 @@
 // past K come back as zeros through the buffer range check.
 //
 // LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r sits at
-// position c ^ f(r), f(r) = g((r >> 1) & 7) ^ (((r >> 4) & 1) << 2), g
-// swapping bits 1 and 2.  A 16-byte LDS read serves 16 lanes per clock on
-// gfx950; with this f every 16-lane group of a fragment read (lanes 0-15,
-// or 0-7 with 32-39, or 0-3/16-19/32-35/48-51, or 0-3/8-11/16-19/24-27)
-// touches 16 distinct bank quads.  A direct-to-LDS load writes lane i's 16
-// bytes at position i of the wave's 1 KiB window, so each lane fetches the
-// global chunk that belongs there.
+// position c ^ f(r), f(r) = (r >> 1) & 7.  A 16-byte LDS read is served 16
+// lanes per clock from 64 banks of 4 bytes, so 16 lanes that share a clock
+// must hit 16 distinct 16-byte slots of a 256-byte bank line.  Which lanes
+// share a clock is not simply lanes 0-15, 16-31, ...; this f was chosen
+// because the hardware's bank-conflict counter reads zero for all four
+// fragment read shapes below (rows r..r+31, chunk pairs c and c+2), and it
+// also is conflict-free under the plain consecutive grouping.  A
+// direct-to-LDS load writes lane i's 16 bytes at position i of the wave's
+// 1 KiB window, so each lane fetches the global chunk that belongs there.
 //
 // The matrix cores compute the transposed tile C^T = B A^T (B's fragment
 // as the first operand): then each lane's register quad holds 4
@@ -47,54 +49,52 @@ constexpr int NT_BM = 256, NT_BN = 256, NT_BK = 128, NT_STAGES = 2;
 constexpr int NT_CHUNKS = NT_BK / 16;                             // 16-byte chunks per row (8)
 constexpr int NT_STAGE_BYTES = (NT_BM + NT_BN) * NT_BK;          // 64 KiB
 constexpr int NT_LOADS = NT_STAGE_BYTES / (GEMM_THREADS * 16);   // 16-byte loads per thread per step (16)
+constexpr int NT_A_BYTES = NT_BM * NT_BK;                        // one stage of A (or B): 32 KiB
+constexpr int NT_READS_PER_SLOT = 2;  // fragment reads issued per MFMA slot (front-loaded)
 
-__device__ __forceinline__ int nt_swz(int r)
-{
-    const int m = (r >> 1) & 7;
-    const int g = (m & 1) | ((m & 2) << 1) | ((m & 4) >> 1);
-    return g ^ (((r >> 4) & 1) << 2);
-}
+__device__ __forceinline__ int nt_swz(int r) { return (r >> 1) & 7; }
 
 template <int AF, int BF> struct Mma32 {
     typedef v16f acc_t;
     static constexpr bool INT_ACC = false;
-    __device__ __forceinline__ static void run(acc_t &c, const v8i &a, const v8i &b)
+    // a = (a0, a1), b = (b0, b1): each operand's 32 bytes as two 16-byte halves.
+    __device__ __forceinline__ static void run(acc_t &c, const u32x4 &a0, const u32x4 &a1, const u32x4 &b0,
+                                               const u32x4 &b1)
     {
+        const v8i a = __builtin_shufflevector((v4i)a0, (v4i)a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i b = __builtin_shufflevector((v4i)b0, (v4i)b1, 0, 1, 2, 3, 4, 5, 6, 7);
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
     }
     __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return __float_as_uint(c[r]); }
 };
 
-template <> struct Mma32<FMT_INT8, FMT_INT8> {
-    typedef v16i acc_t;
-    static constexpr bool INT_ACC = true;
-    __device__ __forceinline__ static void run(acc_t &c, const v8i &a, const v8i &b)
-    {
-        v4i a0 = {a[0], a[1], a[2], a[3]}, a1 = {a[4], a[5], a[6], a[7]};
-        v4i b0 = {b[0], b[1], b[2], b[3]}, b1 = {b[4], b[5], b[6], b[7]};
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1, c, 0, 0, 0);
-    }
-    __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return (uint32_t)c[r]; }
-};
 
 // 32 rows x 64 k fragment for lane l: row (l & 31), k = 64*half +
 // 32*(l >> 5) .. +31 (logical chunks 4*half + 2*(l >> 5) and the next).
 // The two 16-byte LDS reads are issued as inline assembly: the compiler's
 // wait insertion cannot tell that they never touch a stage a direct-to-LDS
 // load is still filling, and would otherwise wait for every load in flight
-// before each read.  Completion is awaited explicitly (nt_wait_lgkm) before
-// the fragments are used.
-__device__ __forceinline__ uint32_t nt_frag_addr(uint32_t lds_base, int row, int chunk)
-{
-    return lds_base + (uint32_t)(row * NT_BK + ((chunk ^ nt_swz(row)) << 4));
-}
+// before each read.  Completion is awaited explicitly (nt_wait_parts) before
+// the fragments are used.  The stage and fragment offsets ride in the
+// instruction's immediate, so a read needs no address arithmetic.
 
+template <int OFF>
 __device__ __forceinline__ u32x4 nt_read16(uint32_t addr)
 {
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset is 16 bits");
     u32x4 x;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(x) : "v"(addr) : "memory");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "n"(OFF) : "memory");
     return x;
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void nt_unroll(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        nt_unroll<B + 1, E>(f);
+    }
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -110,15 +110,13 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
                  : "memory");
 }
 
-__device__ __forceinline__ v8i nt_join(const u32x4 &x, const u32x4 &y)
-{
-    return __builtin_shufflevector((v4i)x, (v4i)y, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
-template <int AF, int BF>
+template <int AF, int BF, bool KTAIL>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 {
     typedef Mma32<BF, AF> MMA;                 // operands swapped: acc holds C^T
+    static_assert(AF != FMT_INT8 && BF != FMT_INT8, "the pipelined kernel is FP8 only");
+    constexpr int RPS = NT_READS_PER_SLOT;
     typedef typename MMA::acc_t acc_t;
     constexpr int WM = NT_BM / 2, WN = NT_BN / 2, TM = WM / 32, TN = WN / 32;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NT_STAGES * NT_STAGE_BYTES];
@@ -139,11 +137,16 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.b + n0 * p.ldb), (short)0, (int)(b_rows > 0 ? b_rows * p.ldb : 0), BUF_WORD3);
 
-    // Load j of this wave covers stage bytes [(jj*4 + wave) * 1024, +1024)
-    // of the A half (j < NT_LOADS/2, jj = j) or the B half (jj = j -
+    // LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB
+    // each, so a fragment read's stage and fragment offsets fit the
+    // instruction's 16-bit immediate offset.
+    //
+    // Load j of this wave covers bytes [(jj*4 + wave) * 1024, +1024) of the
+    // A part of a stage (j < NT_LOADS/2, jj = j) or of the B part (jj = j -
     // NT_LOADS/2).  Lane i lands at position q = (jj*4 + wave)*64 + i
     // (16-byte units): row q/8, swizzled chunk q%8, so it fetches logical
-    // chunk (q%8) ^ f(row).
+    // chunk (q%8) ^ f(row).  The step's k offset travels in the scalar
+    // offset field, so a full step costs no vector instruction per load.
     uint32_t goff[NT_LOADS];
     int kchunk[NT_LOADS];
 #pragma unroll
@@ -156,21 +159,30 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     }
 
     const int K32 = (int)p.K;
-    // Direct-to-LDS load j (0 .. NT_LOADS-1) of `step`.  Chunks past K (only
-    // in a partial last step) get an offset outside the buffer range.
-    auto issue_one = [&](int step, int j) {
-        uint8_t *st = lds + (step % NT_STAGES) * NT_STAGE_BYTES;
-        const int k0 = step * NT_BK;
+    const int nk = (int)((p.K + NT_BK - 1) / NT_BK);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+    const uint32_t lds_wave = lds_base + (uint32_t)wave * 1024u;   // wave-uniform: lands in M0
+    // Direct-to-LDS load j (0 .. NT_LOADS-1) of the step at k offset k0 into
+    // stage S.  Without a K tail every step is whole and k0 rides in the
+    // scalar offset.  With one (KTAIL), chunks at or past K get an offset
+    // outside the buffer range and load as zeros, which also covers the
+    // refills past the last step.
+    auto issue_one = [&](auto S, int k0, int j) {
+        constexpr int STAGE = decltype(S)::value;
         const bool is_a = j < NT_LOADS / 2;
-        const int win = ((j % (NT_LOADS / 2)) * 4 + wave) * 1024 + (is_a ? 0 : NT_BM * NT_BK);
-        uint32_t off = goff[j] + (uint32_t)k0;
-        if (k0 + NT_BK > K32) off = k0 + kchunk[j] < K32 ? off : BUF_OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(st + win), 16, (int)off, 0, 0, 0);
+        const lds_ptr_t dst = (lds_ptr_t)(lds_wave + (uint32_t)((is_a ? 0 : NT_STAGES * NT_A_BYTES) +
+                                                                 STAGE * NT_A_BYTES + (j % (NT_LOADS / 2)) * 4096));
+        if constexpr (!KTAIL) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, dst, 16, (int)goff[j], k0, 0, 0);
+        } else {
+            const uint32_t off = k0 + kchunk[j] < K32 ? goff[j] + (uint32_t)k0 : BUF_OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, dst, 16, (int)off, 0, 0, 0);
+        }
     };
-    auto issue = [&](int step) {
-#pragma unroll
-        for (int j = 0; j < NT_LOADS; ++j) issue_one(step, j);
-    };
+    // k offset of the refill of `step`: steps past the end re-load the last
+    // step (whole K) into a stage nobody reads, so the buffer offsets stay
+    // inside the operands; with a K tail their chunks are all out of range.
+    auto refill_k = [&](int step) { return (KTAIL || step < nk ? step : nk - 1) * NT_BK; };
 
     acc_t acc[TM][TN];
 #pragma unroll
@@ -178,66 +190,97 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
 
-    const int nk = (int)((p.K + NT_BK - 1) / NT_BK);
     const int lr = lane & 31, h = lane >> 5;
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-
-    // LDS address of fragment half t (0..15) of one 64-deep half of `step`:
-    // t/2 selects A fragment 0..3 or B fragment 0..3, t%2 the 16-byte half.
-    auto frag_addr = [&](int step, int half, int t) {
-        const uint32_t as = lds_base + (uint32_t)((step % NT_STAGES) * NT_STAGE_BYTES);
-        const int f = t >> 1;
-        const int chunk = 4 * half + 2 * h + (t & 1);
-        return f < TM ? nt_frag_addr(as, wm0 + f * 32 + lr, chunk)
-                      : nt_frag_addr(as + NT_BM * NT_BK, wn0 + (f - TM) * 32 + lr, chunk);
-    };
-    auto join = [&](u32x4 (&pt)[16], v8i (&af)[TM], v8i (&bf)[TN]) {
+    // Per-lane read bases: a lane reads rows (wm0 | wn0) + f*32 + lr, and
+    // only chunks 4*half + 2*h + e (half, e in {0, 1}).  The swizzle
+    // depends on lr alone (f*32 and the wave offsets are multiples of 32),
+    // so fragment f, stage s adds the immediate s*NT_A_BYTES + f*32*NT_BK.
+    uint32_t rba[2][2], rbb[2][2];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = nt_join(pt[2 * i], pt[2 * i + 1]);
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = nt_join(pt[2 * (TM + j)], pt[2 * (TM + j) + 1]);
-    };
-    constexpr int VM_ONE_STEP = 0x0F70 | (NT_LOADS & 0xF) | ((NT_LOADS >> 4) << 14);
-    v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    u32x4 pt[16];
-    if (nk > 0) {
-        issue(0);
-        issue(1);
-        __builtin_amdgcn_s_waitcnt(VM_ONE_STEP);
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int t = 0; t < 16; ++t) pt[t] = nt_read16(frag_addr(0, 0, t));
-        nt_wait_parts(pt);
-        join(pt, fa0, fb0);
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        // Half 0: MFMAs on set 0, read half 1 into set 1.
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            MMA::run(acc[t >> 2][t & 3], fb0[t & 3], fa0[t >> 2]);
-            pt[t] = nt_read16(frag_addr(kt, 1, t));
-            __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t in_row = (uint32_t)(lr * NT_BK + (((4 * half + 2 * h + e) ^ nt_swz(lr)) << 4));
+            rba[half][e] = lds_base + (uint32_t)(wm0 * NT_BK) + in_row;
+            rbb[half][e] = lds_base + (uint32_t)(NT_STAGES * NT_A_BYTES + wn0 * NT_BK) + in_row;
         }
-        nt_wait_parts(pt);
-        join(pt, fa1, fb1);
-        // This wave is done with stage kt; everyone's loads of step kt+1
-        // have landed once all waves pass the barrier.
+    // Fragment read t (0..15) of one 64-deep half: t/2 selects A fragment
+    // 0..3 or B fragment 0..3, t%2 the 16-byte half.
+    auto read_frag = [&](auto S, auto HALF, auto T) -> u32x4 {
+        constexpr int STAGE = decltype(S)::value, HF = decltype(HALF)::value, t = decltype(T)::value;
+        constexpr int f = t >> 1, e = t & 1;
+        constexpr int off = STAGE * NT_A_BYTES + (f < TM ? f : f - TM) * 32 * NT_BK;
+        return nt_read16<off>(f < TM ? rba[HF][e] : rbb[HF][e]);
+    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    constexpr int VM_ONE_STEP = 0x0F70 | (NT_LOADS & 0xF) | ((NT_LOADS >> 4) << 14);
+    // Two fragment sets of 16 halves each: parts 2i, 2i+1 are A fragment i,
+    // parts 2(TM+j), 2(TM+j)+1 B fragment j.
+    u32x4 f0[16], f1[16];
+    auto mma = [&](u32x4 (&f)[16], int t) {
+        const int i = t >> 2, j = t & 3;
+        MMA::run(acc[i][j], f[2 * (TM + j)], f[2 * (TM + j) + 1], f[2 * i], f[2 * i + 1]);
+    };
+
+    // One k-step worked from stage S (= kt % 2).  Half 0: MFMAs on set 0
+    // while half 1's fragments are read into set 1 (front-loaded,
+    // NT_READS_PER_SLOT per MFMA slot).  Then this wave is done with stage S;
+    // once all waves pass the barrier, everyone's loads of step kt+1 have
+    // landed.  Half 1: MFMAs on set 1 while step kt+1's half-0 fragments are
+    // read from the other stage into set 0 and stage S is refilled with step
+    // kt+2 (two loads per slot, early).
+    auto step = [&](auto S, int kt) {
+        constexpr int STAGE = decltype(S)::value;
+        typedef std::integral_constant<int, 1 - STAGE> SN;
+        nt_unroll<0, 16>([&](auto T) {
+            constexpr int t = decltype(T)::value;
+            mma(f0, t);
+            nt_unroll<0, RPS>([&](auto R) {
+                constexpr int r = t * RPS + decltype(R)::value;
+                if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        nt_wait_parts(f1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __builtin_amdgcn_s_barrier();
-        // Half 1: MFMAs on set 1, read step kt+1's half 0 into set 0, and
-        // refill stage kt with step kt+2 (two loads per slot, early).
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            MMA::run(acc[t >> 2][t & 3], fb1[t & 3], fa1[t >> 2]);
-            pt[t] = nt_read16(frag_addr(kt + 1, 0, t));
-            if (t < NT_LOADS / 2) {
-                issue_one(kt + 2, 2 * t);
-                issue_one(kt + 2, 2 * t + 1);
+        const int k_refill = refill_k(kt + 2);
+        nt_unroll<0, 16>([&](auto T) {
+            constexpr int t = decltype(T)::value;
+            mma(f1, t);
+            nt_unroll<0, RPS>([&](auto R) {
+                constexpr int r = t * RPS + decltype(R)::value;
+                if constexpr (r < 16) f0[r] = read_frag(SN{}, I0{}, std::integral_constant<int, r>{});
+            });
+            if constexpr (t < NT_LOADS / 2) {
+                issue_one(S, k_refill, 2 * t);
+                issue_one(S, k_refill, 2 * t + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
+        });
+        nt_wait_parts(f0);
+    };
+
+    if (nk > 0) {
+#pragma unroll
+        for (int j = 0; j < NT_LOADS; ++j) issue_one(I0{}, 0, j);
+        if (nk > 1) {
+#pragma unroll
+            for (int j = 0; j < NT_LOADS; ++j) issue_one(I1{}, NT_BK, j);
+            __builtin_amdgcn_s_waitcnt(VM_ONE_STEP);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
-        nt_wait_parts(pt);
-        join(pt, fa0, fb0);
+        __builtin_amdgcn_s_barrier();
+        nt_unroll<0, 16>([&](auto T) { f0[decltype(T)::value] = read_frag(I0{}, I0{}, T); });
+        nt_wait_parts(f0);
+    }
+    // Steps past the end read stale fragments that no MFMA uses; the loop
+    // runs two steps per iteration so each step's stage is a constant.
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(I0{}, kt);
+        if (kt + 1 < nk) step(I1{}, kt + 1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -262,14 +305,24 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                     make_uint4(MMA::bits(acc[i][j], 4 * q), MMA::bits(acc[i][j], 4 * q + 1),
                                MMA::bits(acc[i][j], 4 * q + 2), MMA::bits(acc[i][j], 4 * q + 3));
         __syncthreads();
-        constexpr int C4 = WN / 4;
+        // 16 row pieces per lane, read 8 at a time so the LDS latency is
+        // paid twice per slab rather than 16 times.
+        constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
 #pragma unroll 1
-        for (int idx = lane; idx < 32 * C4; idx += 64) {
-            const int rr = idx / C4, c4 = idx - rr * C4;
-            const uint4 w = *reinterpret_cast<const uint4 *>(ep + rr * EP_LD + c4 * 4);
-            const int64_t row = m0 + wm0 + i * 32 + rr;
-            const int64_t col = n0 + wn0 + c4 * 4;
-            if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w, row, col, vmax);
+        for (int g = 0; g < PER_LANE; g += GROUP) {
+            uint4 w[GROUP];
+#pragma unroll
+            for (int u = 0; u < GROUP; ++u) {
+                const int idx = lane + (g + u) * 64;
+                w[u] = *reinterpret_cast<const uint4 *>(ep + (idx / C4) * EP_LD + (idx % C4) * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < GROUP; ++u) {
+                const int idx = lane + (g + u) * 64;
+                const int64_t row = m0 + wm0 + i * 32 + idx / C4;
+                const int64_t col = n0 + wn0 + (idx % C4) * 4;
+                if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w[u], row, col, vmax);
+            }
         }
     }
     if (p.out_amax) {
@@ -287,7 +340,10 @@ hipError_t launch_nt(GemmParams p, hipStream_t s)
     p.tiles_m = (int)((p.M + NT_BM - 1) / NT_BM);
     p.tiles_n = (int)((p.N + NT_BN - 1) / NT_BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
+    if (p.K % NT_BK == 0)
+        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, true>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
     return hipGetLastError();
 }
 

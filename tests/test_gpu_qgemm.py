@@ -282,13 +282,15 @@ def test_large_fp8_sampled(orc):
     print("large_fp8 differing codes:", differ, "of", got.size)
 
 
-@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (2, 2)])
-def test_pipelined_nt_path_ragged(orc, af, bf):
-    """Shapes with at least 256 tiles of 256 x 256 take the pipelined
-    direct-to-LDS kernel: ragged M and N (partial edge tiles) and a K whose
-    last 64-byte step is partial.  Sampled entries include the last rows and
-    columns."""
-    M, N, K = 4133, 4101, 1040
+@pytest.mark.parametrize("af,bf,K", [(0, 0, 1040), (1, 0, 1040), (2, 2, 1040), (0, 0, 1152), (0, 1, 128),
+                                     (1, 1, 256), (0, 0, 384)])
+def test_pipelined_nt_path_ragged(orc, af, bf, K):
+    """FP8 shapes with at least 256 tiles of 256 x 256 take the pipelined
+    direct-to-LDS kernel: ragged M and N (partial edge tiles); K with a
+    partial last 128-byte step (1040), an odd number of whole steps (1152,
+    384), one step (128) and two (256).  INT8 of the same shape takes the
+    general kernel.  Sampled entries include the last rows and columns."""
+    M, N = 4133, 4101
     a = finite_codes(orc, 51, af, M, K, af)
     b = finite_codes(orc, 52, bf, N, K, bf)
     rng = np.random.default_rng(53)
