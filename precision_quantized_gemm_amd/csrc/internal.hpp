@@ -57,6 +57,8 @@ struct GemmParams {
     uint32_t *ws;                   // workspace slot for out_amax
     int a_aligned, b_aligned;       // 16-byte loads allowed
     int out_vec4;                   // 4 consecutive outputs may be stored as one vector
+    int out_vec16;                  // 16 consecutive outputs (16-aligned column) are 16-byte vectors
+    int bias_vec16;                 // bias absent or 16-byte aligned
     int fast;                       // branch-free buffer-load staging applies
     int tiles_m, tiles_n;
 };

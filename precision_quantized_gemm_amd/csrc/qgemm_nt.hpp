@@ -111,6 +111,69 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
 }
 
 
+// Fast-path epilogue of 16 consecutive FP32 accumulators of one row
+// (per-tensor scales, column a multiple of 16, output and bias rows 16-byte
+// aligned, all 16 inside the output): v = acc * sa * sb (+ bias), then one
+// to four 16-byte stores.  Returns the running max |v| as FP32 bits.
+__device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilogue &epi, const uint4 (&w)[4],
+                                               int64_t row, int64_t col, uint32_t vmax)
+{
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[4 * q + 0] = __uint_as_float(w[q].x) * epi.s_ab;
+        v[4 * q + 1] = __uint_as_float(w[q].y) * epi.s_ab;
+        v[4 * q + 2] = __uint_as_float(w[q].z) * epi.s_ab;
+        v[4 * q + 3] = __uint_as_float(w[q].w) * epi.s_ab;
+    }
+    if (p.bias_dt == DT_FP32) {
+        const float4 *b = reinterpret_cast<const float4 *>(static_cast<const float *>(p.bias) + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = b[q];
+            v[4 * q] += x.x; v[4 * q + 1] += x.y; v[4 * q + 2] += x.z; v[4 * q + 3] += x.w;
+        }
+    } else if (p.bias_dt == DT_BF16) {
+        const uint4 *b = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.bias) + col);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint4 x = b[q];
+            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[8 * q + 2 * e] += bf16_lo(xs[e]);
+                v[8 * q + 2 * e + 1] += bf16_hi(xs[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { const uint32_t b = absbits_f32(v[e]); vmax = b > vmax ? b : vmax; }
+    const int64_t o = row * p.ldo + col;
+    if (p.out_dt == DT_E4M3) {
+        const float s = epi.inv_os;
+        uint4 c;
+        c.x = encode4<FMT_E4M3>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+        c.y = encode4<FMT_E4M3>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+        c.z = encode4<FMT_E4M3>(v[8] * s, v[9] * s, v[10] * s, v[11] * s);
+        c.w = encode4<FMT_E4M3>(v[12] * s, v[13] * s, v[14] * s, v[15] * s);
+        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + o) = c;
+    } else if (p.out_dt == DT_BF16) {
+        uint32_t hw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            hw[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * e]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * e + 1]) << 16);
+        uint4 *out = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + o);
+        out[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        out[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    } else {
+        float4 *out = reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    return vmax;
+}
+
 template <int AF, int BF, bool KTAIL>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 {
@@ -288,40 +351,68 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     // Epilogue through LDS, one 32-row slab of the wave tile at a time.
     // Block (i, j) holds C^T: element r of lane l is output row i*32 + l%32,
     // column j*32 + (r/4)*8 + 4*(l/32) + r%4, so register quad q goes to LDS
-    // as one 16-byte write; then each lane takes 4 consecutive columns of a
-    // row for the fused epilogue and a contiguous store.
+    // as one 16-byte write.  Then, on the fast path (whole tile inside the
+    // output, per-tensor scales, 16-byte aligned output rows and bias), each
+    // lane takes 16 consecutive columns of one row (4 pieces per slab) and
+    // writes them with 16-byte stores; otherwise each lane takes 4 columns at
+    // a time through the general epilogue with its bounds checks.  With row
+    // stride EP_LD = 132 words, the 16 lanes that share an LDS clock read 16
+    // distinct bank slots.
     constexpr int EP_LD = WN + 4;                        // padded row, in words
     uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 32 * EP_LD;
     Epilogue epi(p);
+    const bool fast_epi = epi.per_tensor && p.out_vec16 && p.bias_vec16 && m0 + NT_BM <= p.M && n0 + NT_BN <= p.N;
     uint32_t vmax = 0;
-#pragma unroll
+    // The slab loop runs at run time (its body is large); the accumulator
+    // rows go to LDS through compile-time indices so they stay in registers.
+#pragma unroll 1
     for (int i = 0; i < TM; ++i) {
         __syncthreads();
+        nt_unroll<0, TM>([&](auto I) {
+            constexpr int ii = decltype(I)::value;
+            if (i == ii) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
-                    make_uint4(MMA::bits(acc[i][j], 4 * q), MMA::bits(acc[i][j], 4 * q + 1),
-                               MMA::bits(acc[i][j], 4 * q + 2), MMA::bits(acc[i][j], 4 * q + 3));
-        __syncthreads();
-        // 16 row pieces per lane, read 8 at a time so the LDS latency is
-        // paid twice per slab rather than 16 times.
-        constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
-#pragma unroll 1
-        for (int g = 0; g < PER_LANE; g += GROUP) {
-            uint4 w[GROUP];
-#pragma unroll
-            for (int u = 0; u < GROUP; ++u) {
-                const int idx = lane + (g + u) * 64;
-                w[u] = *reinterpret_cast<const uint4 *>(ep + (idx / C4) * EP_LD + (idx % C4) * 4);
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
+                            make_uint4(MMA::bits(acc[ii][j], 4 * q), MMA::bits(acc[ii][j], 4 * q + 1),
+                                       MMA::bits(acc[ii][j], 4 * q + 2), MMA::bits(acc[ii][j], 4 * q + 3));
             }
+        });
+        __syncthreads();
+        if (fast_epi) {
+            // Piece u of this lane: slab row (lane + 64u) / 8, columns
+            // 16 * (lane % 8) .. +15 of the wave's 128.
+            uint4 w[4][4];
 #pragma unroll
-            for (int u = 0; u < GROUP; ++u) {
-                const int idx = lane + (g + u) * 64;
-                const int64_t row = m0 + wm0 + i * 32 + idx / C4;
-                const int64_t col = n0 + wn0 + (idx % C4) * 4;
-                if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w[u], row, col, vmax);
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    w[u][v] = *reinterpret_cast<const uint4 *>(ep + ((lane >> 3) + 8 * u) * EP_LD + (lane & 7) * 16 + 4 * v);
+            const int64_t col = n0 + wn0 + (lane & 7) * 16;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t row = m0 + wm0 + i * 32 + (lane >> 3) + 8 * u;
+                vmax = nt_store16(p, epi, w[u], row, col, vmax);
+            }
+        } else {
+            constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
+#pragma unroll 1
+            for (int g = 0; g < PER_LANE; g += GROUP) {
+                uint4 w[GROUP];
+#pragma unroll
+                for (int u = 0; u < GROUP; ++u) {
+                    const int idx = lane + (g + u) * 64;
+                    w[u] = *reinterpret_cast<const uint4 *>(ep + (idx / C4) * EP_LD + (idx % C4) * 4);
+                }
+#pragma unroll
+                for (int u = 0; u < GROUP; ++u) {
+                    const int idx = lane + (g + u) * 64;
+                    const int64_t row = m0 + wm0 + i * 32 + idx / C4;
+                    const int64_t col = n0 + wn0 + (idx % C4) * 4;
+                    if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w[u], row, col, vmax);
+                }
             }
         }
     }

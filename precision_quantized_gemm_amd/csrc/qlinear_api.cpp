@@ -213,6 +213,10 @@ ql::GemmParams make_gemm(const GemmArgs &g, uint32_t *slot)
     p.fast = a_ok && b_ok;
     const int eb = out_elem_bytes(g.out_dt);
     p.out_vec4 = (reinterpret_cast<uintptr_t>(g.out) % (uintptr_t)(4 * eb)) == 0 && g.ldo % 4 == 0;
+    // 16 consecutive outputs of a row (16-column aligned) are whole 16-byte
+    // vectors, and so are 16 consecutive bias entries.
+    p.out_vec16 = aligned16(g.out) && (g.ldo * eb) % 16 == 0;
+    p.bias_vec16 = p.bias == nullptr || aligned16(p.bias);
     return p;
 }
 

@@ -309,3 +309,51 @@ def test_pipelined_nt_path_ragged(orc, af, bf, K):
     out = run_gpu(a, af, 0, b, bf, 0, K, [0.004], 0, [0.5], 0, bias=bias, out_dtype="bf16")
     print("nt ragged", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, bias=bias_of(bias, ns),
                                    what=f"nt ragged fmt={af},{bf}"))
+
+
+@pytest.mark.parametrize("out_dtype,bias_kind,af,bf", [("bf16", "fp32", 0, 0), ("fp32", "bf16", 1, 0),
+                                                       ("e4m3", None, 0, 0), ("e4m3", "fp32", 0, 1)])
+def test_pipelined_fast_epilogue(orc, out_dtype, bias_kind, af, bf):
+    """Whole tiles of the pipelined kernel with per-tensor scales and 16-byte
+    aligned output rows take the 16-column epilogue; the ragged edge tiles
+    take the general one.  Every output dtype and bias dtype, sampled
+    entries on both sides of the edge, and out_amax equal to max |v| of the
+    FP32 values of the same product."""
+    M, N, K = 4096 + 37, 4096 + 48, 256
+    a = finite_codes(orc, 61, af, M, K, af)
+    b = finite_codes(orc, 62, bf, N, K, bf)
+    sa, sb = np.float32(0.01), np.float32(0.02)
+    dev = "cuda"
+    b32 = synth.normal(63, 0, N, 0.5)
+    if bias_kind == "bf16":
+        bias_t = torch.from_numpy(b32).to(torch.bfloat16)
+    elif bias_kind == "fp32":
+        bias_t = torch.from_numpy(b32)
+    else:
+        bias_t = None
+    bias_vals = None if bias_t is None else bias_t.float().numpy()
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    ts = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)
+    tbias = None if bias_t is None else bias_t.to(dev)
+    ref32, amax32 = q.qgemm(ta, FMT[af], tb, FMT[bf], ts(sa), ts(sb), bias=tbias, out_dtype="fp32", out_amax=True)
+    torch.cuda.synchronize()
+    assert amax32.item() == ref32.abs().max().item()
+    os_ = np.float32(amax32.item() / 448.0 * 0.5) if out_dtype == "e4m3" else None
+    out, amax = q.qgemm(ta, FMT[af], tb, FMT[bf], ts(sa), ts(sb), bias=tbias, out_dtype=out_dtype,
+                        out_scale=None if os_ is None else ts(os_), out_amax=True)
+    torch.cuda.synchronize()
+    assert amax.item() == amax32.item()
+    rows = np.array([0, 255, 2048, 4095, 4096, M - 1])
+    cols = np.array([0, 15, 16, 4095, 4096, N - 1])
+    rng = np.random.default_rng(64)
+    ms = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 2000)])
+    ns = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 2000)])
+    ms, ns = ms.astype(np.int64), ns.astype(np.int64)
+    acc, S, _, H, v, sasb = oracle_entries(orc, a, af, 0, b, bf, 0, K, ms, ns, [sa], 0, [sb], 0, bias_vals)
+    got = out_values(out.cpu())[ms, ns]
+    if out_dtype == "e4m3":
+        differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, bias=bias_of(bias_vals, ns), what="fast epi")
+        print("fast epilogue e4m3 differing codes:", differ, "of", got.size)
+    else:
+        print("fast epilogue", check_float(got, v, S, H, sasb, K, bias=bias_of(bias_vals, ns),
+                                           what=f"fast epi {out_dtype}"))
