@@ -38,6 +38,11 @@ sys.path.insert(0, str(ROOT))
 METRIC = "qgemm TFLOP/s & % dense FP8/INT8 MFMA peak; quantize GB/s & % HBM peak"
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 matrix-core peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak
+# Profiler HBM byte counters of the GEMM kernel at this workload, per launch,
+# already scaled by the copy calibration, with the hash of the kernel
+# sources they were taken on; used only while the sources still match.
+TRAFFIC_FILE = ROOT / "profiles" / "qgemm_nt_e4m3_large_fp8_traffic.json"
+KERNEL_SOURCES = ["qgemm_nt.hpp", "qgemm_impl.hpp", "qdev.hpp", "internal.hpp", "qgemm_e4m3_e4m3.hip"]
 
 
 def parse():
@@ -48,7 +53,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4, help="output rows in the oracle GEMM sample")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="output rows in the oracle GEMM sample")
+    ap.add_argument("--cpu-cols", type=int, default=4096, help="output columns in the oracle GEMM sample")
     return ap.parse_args()
 
 
@@ -69,13 +75,14 @@ def time_events(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
-def cpu_baseline(a_cpu, b_cpu, M, N, K, rows):
+def cpu_baseline(a_cpu, b_cpu, M, N, K, rows, cols):
     """Oracle timing on a bounded sample, scaled to one full step.
 
-    Sample: the per-tensor E4M3 quantize of `rows_q` rows of a and of b, and
-    the exact GEMM of `rows` full output rows (rows x N entries x K), split
-    over the host's threads.  Step estimate = per-element quantize time x
-    (M*K + N*K) + per-MAC GEMM time x M*N*K.
+    Sample (roughly 10-30 s of host work): the per-tensor E4M3 quantize of
+    the first 4096 rows of a and of b (one thread: the oracle quantize is a
+    single call), and the exact GEMM of `rows` x `cols` outputs over the full
+    K, split over the host's threads.  Step estimate = per-element quantize
+    time x (M*K + N*K) + per-MAC GEMM time x M*N*K.
     """
     import numpy as np
 
@@ -83,18 +90,17 @@ def cpu_baseline(a_cpu, b_cpu, M, N, K, rows):
     from precision_quantized_gemm_amd import synth
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    rows_q = 256
+    rows_q = 4096
     xa = synth.bf16_bits(a_cpu[:rows_q])
     xb = synth.bf16_bits(b_cpu[:rows_q])
     t0 = time.perf_counter()
     qa, sa, _ = oracle.quantize(xa, oracle.PER_TENSOR, oracle.E4M3)
     qb, sb, _ = oracle.quantize(xb, oracle.PER_TENSOR, oracle.E4M3)
-    tq = (time.perf_counter() - t0) / (2 * rows_q * K)
-    # GEMM sample: `rows` output rows against the first rows_q rows of b
-    # (the per-entry cost does not depend on which rows are used).
-    ms = np.repeat(np.arange(rows), rows_q).astype(np.int64)
-    ns = np.tile(np.arange(rows_q), rows).astype(np.int64)
-    chunks = np.array_split(np.arange(ms.size), threads)
+    tq_wall = time.perf_counter() - t0
+    tq = tq_wall / (2 * rows_q * K)
+    ms = np.repeat(np.arange(rows), cols).astype(np.int64)
+    ns = np.tile(np.arange(cols), rows).astype(np.int64)
+    chunks = np.array_split(np.arange(ms.size), threads * 4)
 
     def work(idx):
         oracle.qgemm_entries(qa, 0, 0, qb, 0, 0, K, ms[idx], ns[idx], with_bound=False)
@@ -106,10 +112,30 @@ def cpu_baseline(a_cpu, b_cpu, M, N, K, rows):
     tmac = tg_wall / (ms.size * K)
     step_s = tq * (M * K + N * K) + tmac * M * N * K
     return dict(value=2.0 * M * N * K / step_s / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=(f"quantize of {rows_q} rows of a and of b ({2 * rows_q * K} elements, 1 thread) and the "
-                        f"exact GEMM of {rows}x{rows_q} outputs x K={K} ({ms.size * K} MACs, {threads} threads); "
-                        f"scaled to the full {M}x{N}x{K} step"),
+                sample=(f"quantize of the first {rows_q} rows of a and of b ({2 * rows_q * K} elements, "
+                        f"1 thread, {tq_wall:.1f} s) and the exact GEMM of {rows}x{cols} outputs x K={K} "
+                        f"({ms.size * K} MACs, {threads} threads, {tg_wall:.1f} s); scaled to the full "
+                        f"{M}x{N}x{K} step"),
                 step_seconds_estimate=step_s)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "precision_quantized_gemm_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when the kernel sources changed since it was taken."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    t = json.loads(TRAFFIC_FILE.read_text())
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t["hbm_bytes_per_launch"]
 
 
 def copy_calibration(torch, dev, nbytes=1 << 30, reps=10):
@@ -224,7 +250,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(a_cpu, b_cpu, M, N, K, args.cpu_rows)
+        cpu = cpu_baseline(a_cpu, b_cpu, M, N, K, args.cpu_rows, args.cpu_cols)
 
     line = {
         "metric": METRIC,
@@ -251,7 +277,7 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
+            "traffic": gemm_traffic(),
             "kernel": "qgemm_nt_kernel<E4M3,E4M3> (256x256x128 tiles)",
             "ms_per_launch": round(ms_gemm, 5),
             "per_launch_flops": flops,
