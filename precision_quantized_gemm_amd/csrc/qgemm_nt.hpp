@@ -292,7 +292,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     // once all waves pass the barrier, everyone's loads of step kt+1 have
     // landed.  Half 1: MFMAs on set 1 while step kt+1's half-0 fragments are
     // read from the other stage into set 0 and stage S is refilled with step
-    // kt+2 (two loads per slot, early).
+    // kt+2 (one load per slot: bursts overflow the texture address queue and
+// stall the wave).
     auto step = [&](auto S, int kt) {
         constexpr int STAGE = decltype(S)::value;
         typedef std::integral_constant<int, 1 - STAGE> SN;
@@ -316,10 +317,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                 constexpr int r = t * RPS + decltype(R)::value;
                 if constexpr (r < 16) f0[r] = read_frag(SN{}, I0{}, std::integral_constant<int, r>{});
             });
-            if constexpr (t < NT_LOADS / 2) {
-                issue_one(S, k_refill, 2 * t);
-                issue_one(S, k_refill, 2 * t + 1);
-            }
+            issue_one(S, k_refill, t);
             __builtin_amdgcn_sched_barrier(0);
         });
         nt_wait_parts(f0);
