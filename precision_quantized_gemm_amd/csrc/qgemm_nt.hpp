@@ -346,55 +346,74 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
-    // Epilogue through LDS, one 32-row slab of the wave tile at a time.
-    // Block (i, j) holds C^T: element r of lane l is output row i*32 + l%32,
-    // column j*32 + (r/4)*8 + 4*(l/32) + r%4, so register quad q goes to LDS
-    // as one 16-byte write.  Then, on the fast path (whole tile inside the
-    // output, per-tensor scales, 16-byte aligned output rows and bias), each
-    // lane takes 16 consecutive columns of one row (4 pieces per slab) and
-    // writes them with 16-byte stores; otherwise each lane takes 4 columns at
-    // a time through the general epilogue with its bounds checks.  With row
-    // stride EP_LD = 132 words, the 16 lanes that share an LDS clock read 16
-    // distinct bank slots.
-    constexpr int EP_LD = WN + 4;                        // padded row, in words
-    uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 32 * EP_LD;
+    // Epilogue.  Block (i, j) holds C^T: element r of lane l is output row
+    // i*32 + l%32, column j*32 + (r/4)*8 + 4*(l/32) + r%4.
+    //
+    // Fast path (whole tile inside the output, per-tensor scales, 16-byte
+    // aligned output and bias rows): straight from registers.  Swapping the
+    // upper half-wave of register quads 0 and 1 with the lower half-wave of
+    // quads 2 and 3 (v_permlane32_swap) leaves lane l with the 16
+    // consecutive columns 16*(l/32) .. +15 of its row, in quad order
+    // 0, 2, 1, 3, which then go out as 16-byte stores.
+    //
+    // Otherwise through LDS, one 32-row slab of the wave tile at a time:
+    // register quad q goes to LDS as one 16-byte write, then each lane takes
+    // 4 columns at a time through the general epilogue with its bounds
+    // checks.  With row stride EP_LD = 132 words, the 16 lanes that share an
+    // LDS clock touch 16 distinct bank slots.
     Epilogue epi(p);
     const bool fast_epi = epi.per_tensor && p.out_vec16 && p.bias_vec16 && m0 + NT_BM <= p.M && n0 + NT_BN <= p.N;
     uint32_t vmax = 0;
-    // The slab loop runs at run time (its body is large); the accumulator
-    // rows go to LDS through compile-time indices so they stay in registers.
+    if (fast_epi) {
+        // One block per iteration at run time (keeps the code and register
+        // pressure small); the block's accumulators are picked out through
+        // compile-time indices.
 #pragma unroll 1
-    for (int i = 0; i < TM; ++i) {
-        __syncthreads();
-        nt_unroll<0, TM>([&](auto I) {
-            constexpr int ii = decltype(I)::value;
-            if (i == ii) {
+        for (int b = 0; b < TM * TN; ++b) {
+            const int i = b / TN, j = b % TN;
+            uint32_t x[16];
+            nt_unroll<0, TM * TN>([&](auto B) {
+                constexpr int bb = decltype(B)::value;
+                if (b == bb) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                    for (int r = 0; r < 16; ++r) x[r] = MMA::bits(acc[bb / TN][bb % TN], r);
+                }
+            });
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
-                            make_uint4(MMA::bits(acc[ii][j], 4 * q), MMA::bits(acc[ii][j], 4 * q + 1),
-                                       MMA::bits(acc[ii][j], 4 * q + 2), MMA::bits(acc[ii][j], 4 * q + 3));
+            for (int r = 0; r < 4; ++r) {
+                const auto s02 = __builtin_amdgcn_permlane32_swap(x[r], x[8 + r], false, false);
+                x[r] = s02[0]; x[8 + r] = s02[1];
+                const auto s13 = __builtin_amdgcn_permlane32_swap(x[4 + r], x[12 + r], false, false);
+                x[4 + r] = s13[0]; x[12 + r] = s13[1];
             }
-        });
-        __syncthreads();
-        if (fast_epi) {
-            // Piece u of this lane: slab row (lane + 64u) / 8, columns
-            // 16 * (lane % 8) .. +15 of the wave's 128.
-            uint4 w[4][4];
+            const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
+                                make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
+            const int64_t row = m0 + wm0 + i * 32 + lr;
+            const int64_t col = n0 + wn0 + j * 32 + h * 16;
+            vmax = nt_store16(p, epi, w, row, col, vmax);
+        }
+    } else {
+        constexpr int EP_LD = WN + 4;                    // padded row, in words
+        uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 32 * EP_LD;
+        // The slab loop runs at run time (its body is large); the accumulator
+        // rows go to LDS through compile-time indices so they stay in
+        // registers.
+#pragma unroll 1
+        for (int i = 0; i < TM; ++i) {
+            __syncthreads();
+            nt_unroll<0, TM>([&](auto I) {
+                constexpr int ii = decltype(I)::value;
+                if (i == ii) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+                    for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    w[u][v] = *reinterpret_cast<const uint4 *>(ep + ((lane >> 3) + 8 * u) * EP_LD + (lane & 7) * 16 + 4 * v);
-            const int64_t col = n0 + wn0 + (lane & 7) * 16;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t row = m0 + wm0 + i * 32 + (lane >> 3) + 8 * u;
-                vmax = nt_store16(p, epi, w[u], row, col, vmax);
-            }
-        } else {
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
+                                make_uint4(MMA::bits(acc[ii][j], 4 * q), MMA::bits(acc[ii][j], 4 * q + 1),
+                                           MMA::bits(acc[ii][j], 4 * q + 2), MMA::bits(acc[ii][j], 4 * q + 3));
+                }
+            });
+            __syncthreads();
             constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
 #pragma unroll 1
             for (int g = 0; g < PER_LANE; g += GROUP) {
