@@ -79,6 +79,8 @@ def _load():
     lib.orc_amax_raw.restype = None
     lib.orc_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, i64, vp, vp]
     lib.orc_quantize.restype = None
+    lib.orc_ring_update.argtypes = [vp, i64, i64, i32, i32, flt]
+    lib.orc_ring_update.restype = None
     lib.orc_qgemm_entries.argtypes = [vp, i32, i32, i64, vp, i32, i32, i64, i64, vp, vp, i64, vp, vp, vp, vp, i32, i32]
     lib.orc_qgemm_entries.restype = None
     lib.orc_epilogue.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp]
@@ -167,6 +169,25 @@ def quantize(x: np.ndarray, gran: int, fmt: int, scale_in: np.ndarray | None = N
                          _ptr(sin) if sin is not None else None,
                          _ptr(codes), cols, _ptr(scale), _ptr(amax))
     return codes, scale, amax
+
+
+def quantize_ring(x: np.ndarray, fmt: int, ring: np.ndarray, idx: int, margin: int = 0):
+    """One delayed-scaling quantize with an amax history ring.
+
+    ``ring`` is float32 ``[hist_len + 1]`` = ``[hist | scale]`` and is updated
+    in place.  Returns ``(codes, scale_used, amax)``: the codes use the
+    ring's scale as it was on entry (``scale_used``), ``amax`` (floored) is
+    stored at ``hist[idx]`` and the ring's scale becomes the next step's.
+    """
+    if ring.dtype != np.float32 or ring.ndim != 1 or ring.size < 2:
+        raise ValueError("ring must be a 1-D float32 array [hist | scale]")
+    hist_len = ring.size - 1
+    if not 0 <= idx < hist_len:
+        raise ValueError("idx must index the history")
+    scale_used = np.float32(ring[hist_len])
+    codes, _, amax = quantize(x, PER_TENSOR, fmt, scale_in=np.array([scale_used], np.float32))
+    _load().orc_ring_update(_ptr(ring), hist_len, idx, margin, fmt, float(amax[0]))
+    return codes, scale_used, np.float32(amax[0])
 
 
 # Matrix-core alignment used by qgemm_entries' H output: groups of 8

@@ -235,6 +235,30 @@ void orc_quantize(const void *x, int dt, int64_t rows, int64_t cols, int64_t ldx
 }
 
 /* ------------------------------------------------------------------------ */
+/* Delayed-scaling amax history ("scale ring").  [FP8PY] linear_forward_fp8
+ * and linear_backward_fp8 docstrings: the ring is a float32 buffer holding
+ * an amax history and the scale; the quantize of step t casts with the
+ * scale already in the ring (delayed scaling), stores the amax it measures
+ * at hist[idx], and publishes the scale for the next step.  The page gives
+ * no formula for that scale; the reading taken here (the usual delayed
+ * scaling rule) is
+ *     next = fl32( fl32(max_i hist[i] / qmax) * 2^margin )
+ * with the measured amax floored as in current scaling, so an all-zero
+ * history still gives a positive step.  ring = [hist (hist_len) | scale].
+ * This function does the bookkeeping after the cast; the cast itself is
+ * orc_quantize with scale_in = the ring's old scale.                       */
+void orc_ring_update(float *ring, int64_t hist_len, int64_t idx, int margin, int fmt, float amax)
+{
+    double qmax = orc_qmax(fmt);
+    ring[idx] = amax;
+    double m = 0.0;
+    for (int64_t i = 0; i < hist_len; ++i)
+        if ((double)ring[i] > m) m = ring[i];
+    float step = (float)(m / qmax);
+    ring[hist_len] = (float)ldexp((double)step, margin);
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM.  C[m,n] = sum_k dec(A[m,k]) * dec(B[n,k])  ([SCMP] "API": a @ b.T;
  * [FP8PY] fp8_gemm: FP32 accumulation of a @ b).  A is [M,K], B is [N,K];
  * K-major means k is the contiguous index (A[m*lda+k]), MN-major means m (or

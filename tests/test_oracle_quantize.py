@@ -180,3 +180,44 @@ def test_row_index_and_leading_dim(orc):
     c2, s2, a2 = orc.quantize(xs, orc.PER_ROW, orc.E4M3)
     assert np.array_equal(c2, c[[2, 1, 0, 3, 4]]) and np.array_equal(s2, s[[2, 1, 0, 3, 4]])
     assert s[2] > 4 * s[1]
+
+
+def _ring_steps():
+    for parts in read_golden("ring_handworked.txt"):
+        cols = " ".join(parts[1:]).split("|")
+        idx, margin = map(int, cols[0].split())
+        x = np.array([list(map(float, cols[1].split()))], np.float32)
+        codes = [int(c, 16) for c in cols[2].split()]
+        scale_used, amax = map(float, cols[3].split())
+        hist = list(map(float, cols[4].split()))
+        scale = float(cols[5])
+        yield idx, margin, x, codes, scale_used, amax, hist, scale
+
+
+def test_ring_handworked_sequence(orc):
+    """Delayed scaling with an amax history ring: the hand-worked sequence
+    (saturating casts with the old scale, the window max falling out of the
+    history, a margin) from tests/golden/ring_handworked.txt."""
+    ring = np.array([0, 0, 0, 1], np.float32)
+    for idx, margin, x, codes, scale_used, amax, hist, scale in _ring_steps():
+        got, su, am = orc.quantize_ring(x, 0, ring, idx, margin)
+        assert list(got[0]) == codes
+        assert su == np.float32(scale_used) and am == np.float32(amax)
+        assert list(ring[:3]) == [np.float32(h) for h in hist]
+        assert ring[3] == np.float32(scale)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("margin", [-3, 0, 2])
+def test_ring_zero_history_closed_form(orc, fmt, margin):
+    """An all-zero input into an all-zero history: the stored amax is the
+    floor and the next scale is fl32(floor / qmax) * 2^margin."""
+    ring = np.zeros(5, np.float32)
+    ring[4] = 1.0
+    x = np.zeros((2, 7), np.float32)
+    codes, su, am = orc.quantize_ring(x, fmt, ring, 2, margin)
+    floor = orc.amax_floor(fmt)
+    assert am == floor and ring[2] == floor and su == np.float32(1.0)
+    assert np.all((codes == 0) | (codes == 0x80) if fmt != 2 else codes == 0)
+    expect = np.float32(np.float32(np.float64(floor) / orc.qmax(fmt)) * np.float32(2.0 ** margin))
+    assert ring[4] == expect
