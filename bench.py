@@ -247,6 +247,30 @@ def main():
     qa_gbps = qa_bytes5 / (ms_qa * 1e-3) / 1e9
     qb_gbps = qb_bytes5 / (ms_qb * 1e-3) / 1e9
 
+    # Single-pass delayed scaling through an amax history ring on the same
+    # a (one read of BF16 x, one code byte written: 3 B/elem), timed on its
+    # own after the step.
+    ring = torch.zeros(17, dtype=torch.float32, device=dev)
+    ring[-1] = 1.0
+    su, am = f1(), f1()
+    ring_idx = [0]
+
+    def qa_ring():
+        q.ql_quantize_ring(P(a), _lib.QL_DT_BF16, M, K, K, _lib.QL_FMT_E4M3, P(ring), 16, ring_idx[0] % 16, 0,
+                           P(x_q), K, P(su), P(am), P(ws), stream)
+        ring_idx[0] += 1
+
+    for _ in range(3):
+        qa_ring()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        qa_ring()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_ring = e0.elapsed_time(e1) / args.steps
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -289,6 +313,10 @@ def main():
             "a_GBps_3B_per_elem": round(qa_bytes3 / (ms_qa * 1e-3) / 1e9, 1),
             "b_GBps_5B_per_elem": round(qb_gbps, 1),
             "a_frac_hbm_peak_5B": round(qa_gbps / PEAK_HBM_GBPS, 4),
+            "a_ring_ms": round(ms_ring, 5),
+            "a_ring_GBps_3B_per_elem": round(qa_bytes3 / (ms_ring * 1e-3) / 1e9, 1),
+            "a_ring_frac_hbm_peak": round(qa_bytes3 / (ms_ring * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "a_ring_note": "ql_quantize_ring (delayed scaling, 16-entry history), back to back on a",
             "peak_GBps": PEAK_HBM_GBPS,
         },
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)

@@ -130,6 +130,43 @@ ql_status ql_quantize(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, 
                       void *ws, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ql_quantize_ring -- per-tensor delayed scaling with an amax history ring.
+ *
+ * [FP8PY] linear_forward_fp8 / linear_backward_fp8 docstrings: delayed
+ * scaling keeps a float32 buffer with an amax history and the scale, and
+ * the quantize kernel itself finalizes it (the measured amax goes to
+ * hist[idx], the next step's scale is published on device, no extra
+ * launch).  The page packs a counter into the same buffer; here the
+ * workspace carries the last-workgroup election, so the ring is
+ * [hist | scale].  The page gives no formula for the next scale; this
+ * library publishes fl32(fl32(max(hist) / qmax) * 2^margin).
+ *
+ *   x        [rows, cols], leading dimension ldx >= cols; BF16 or FP32.
+ *   fmt      E4M3, E5M2 or INT8.
+ *   ring     float32 [hist_len + 1] = [hist | scale], device memory owned
+ *            by the caller, read and updated in place.  Initialize the
+ *            history to 0 and the scale to a starting step (e.g. 1).
+ *   hist_len 1 .. 2^20.  idx: slot of this call's amax, 0 <= idx < hist_len
+ *            (the caller advances it, usually modulo hist_len).
+ *   margin   -64 .. 64: the published step is scaled by 2^margin.
+ *   x_q      [rows, cols] codes (ldq >= cols), cast with the ring's scale
+ *            as it was on entry: sat(RNE(x / scale)) as in ql_quantize.
+ *   scale_used [1], optional: that scale, for the GEMM that consumes x_q
+ *            (the ring's scale has moved on when the call completes).
+ *   amax_out [1], optional: max(max|x|, floor) of this x.
+ *   ws       workspace (required).
+ * One pass over x: 2 bytes (BF16) or 4 read and 1 written per element.
+ * Calls that share a ring must be ordered (same stream); they also share
+ * the workspace rule of every call.
+ * Errors: as ql_quantize, plus QL_ERR_NULL (no ring) and QL_ERR_VALUE
+ * (hist_len, idx or margin out of range).
+ * ---------------------------------------------------------------------- */
+ql_status ql_quantize_ring(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
+                           ql_qfmt fmt, float *ring, int64_t hist_len, int64_t idx, int margin,
+                           void *x_q, int64_t ldq, float *scale_used, float *amax_out,
+                           void *ws, void *stream);
+
+/* ------------------------------------------------------------------------
  * ql_qgemm -- out = (A_q @ B_q^T) * sa * sb (+ bias), FP32 or INT32
  * accumulation, BF16 / FP32 / E4M3 / INT32 output.
  *

@@ -51,6 +51,8 @@ def load():
     lib.ql_workspace_init.restype = i32
     lib.ql_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, i64, vp, vp, vp, vp]
     lib.ql_quantize.restype = i32
+    lib.ql_quantize_ring.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, i64, i32, vp, i64, vp, vp, vp, vp]
+    lib.ql_quantize_ring.restype = i32
     lib.ql_qgemm.argtypes = [vp, i32, i32, i64, vp, i32, i32, i64, i64, i64, i64,
                              vp, i32, vp, i32, vp, i32, vp, i32, i64, vp, vp, vp, vp]
     lib.ql_qgemm.restype = i32
@@ -89,6 +91,12 @@ def ql_quantize(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_o
                 ws, stream=0) -> None:
     _check(load().ql_quantize(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq,
                               scale_out, amax_out, ws, stream), "ql_quantize")
+
+
+def ql_quantize_ring(x, x_dt, rows, cols, ldx, fmt, ring, hist_len, idx, margin, x_q, ldq, scale_used,
+                     amax_out, ws, stream=0) -> None:
+    _check(load().ql_quantize_ring(x, x_dt, rows, cols, ldx, fmt, ring, hist_len, idx, margin, x_q, ldq,
+                                   scale_used, amax_out, ws, stream), "ql_quantize_ring")
 
 
 def ql_qgemm(a_q, a_fmt, a_lay, lda, b_q, b_fmt, b_lay, ldb, M, N, K, sa, sa_gran, sb, sb_gran,

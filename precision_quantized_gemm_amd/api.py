@@ -101,6 +101,32 @@ def quantize(x: torch.Tensor, granularity="per_tensor", fmt="e4m3", scale_in=Non
     return x_q, scale, amax
 
 
+def quantize_ring(x: torch.Tensor, fmt, ring: torch.Tensor, idx: int, margin: int = 0, ws=None):
+    """Per-tensor delayed scaling with an amax history ring.
+
+    ``ring`` is a float32 device tensor ``[hist_len + 1]`` = ``[hist | scale]``
+    updated in place.  Returns ``(x_q, scale_used, amax)``: the codes use the
+    ring's scale as it was on entry (``scale_used``, for the GEMM that
+    consumes them); ``amax`` is stored at ``hist[idx]`` and the ring's scale
+    becomes fl32(max(hist)/qmax) * 2^margin.
+    """
+    if x.dtype not in _IN_DT:
+        raise TypeError(f"quantize_ring requires bf16 or fp32 input, got {x.dtype}")
+    if ring.dtype != torch.float32 or ring.dim() != 1 or not ring.is_contiguous():
+        raise TypeError("ring must be a contiguous 1-D float32 tensor [hist | scale]")
+    f = _enum(FMTS, fmt, "format")
+    rows, cols, ldx = _rows_view(x)
+    x_q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scale_used = torch.empty(1, dtype=torch.float32, device=x.device)
+    amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(x.device)
+    _lib.ql_quantize_ring(x.data_ptr(), _IN_DT[x.dtype], rows, cols, ldx, f, ring.data_ptr(), ring.numel() - 1,
+                          idx, margin, x_q.data_ptr(), cols, scale_used.data_ptr(), amax.data_ptr(), _ptr(ws),
+                          _stream())
+    return x_q, scale_used, amax
+
+
 def qgemm(a_q, a_fmt, b_q, b_fmt, sa, sb, *, a_layout="k_major", b_layout="k_major",
           sa_granularity="per_tensor", sb_granularity="per_tensor", bias=None,
           out_dtype="bf16", out_scale=None, out_amax=False, K=None, ws=None):

@@ -36,6 +36,14 @@ struct QzParams {
     int per_row;
     int vec_rows;             // per-row kernel may use 16-byte units
     int delayed;
+    // Delayed scaling with an amax history ring [hist (hist_len) | scale]:
+    // the cast reads the scale from ring[hist_len] (scale_src), and the last
+    // workgroup stores amax at hist[ring_idx], writes the scale it used to
+    // scale_used and publishes fl32(max(hist)/qmax) * 2^margin.
+    float *ring;
+    int64_t hist_len, ring_idx;
+    int margin;
+    float *scale_used;
 };
 
 hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s);

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     auto issue_one = [&](auto S, int k0, int j) {
         constexpr int STAGE = decltype(S)::value;
         const bool is_a = j < NT_LOADS / 2;
-        const lds_ptr_t dst = (lds_ptr_t)(lds_wave + (uint32_t)((is_a ? 0 : NT_STAGES * NT_A_BYTES) +
+        const lds_ptr_t dst = (lds_ptr_t)(uintptr_t)(lds_wave + (uint32_t)((is_a ? 0 : NT_STAGES * NT_A_BYTES) +
                                                                  STAGE * NT_A_BYTES + (j % (NT_LOADS / 2)) * 4096));
         if constexpr (!KTAIL) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, dst, 16, (int)goff[j], k0, 0, 0);

@@ -63,6 +63,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t INT8_K_MAX = 133144;          // K * 127^2 <= 2^31 - 1
 constexpr int64_t MAX_DIM = (int64_t)1 << 40;   // keeps every byte offset far inside int64
+constexpr int64_t RING_MAX_HIST = (int64_t)1 << 20;
+constexpr int RING_MAX_MARGIN = 64;
 
 bool valid_fmt(int f) { return f == QL_FMT_E4M3 || f == QL_FMT_E5M2 || f == QL_FMT_INT8; }
 bool valid_gran(int g) { return g == QL_PER_TENSOR || g == QL_PER_ROW; }
@@ -245,6 +247,33 @@ ql_status ql_quantize(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, 
     uint32_t *slot = ws ? ql::ws_slot(ws, ql::WS_SLOT_QA) : nullptr;
     ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, amax_out, slot);
     return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+ql_status ql_quantize_ring(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
+                           ql_qfmt fmt, float *ring, int64_t hist_len, int64_t idx, int margin,
+                           void *x_q, int64_t ldq, float *scale_used, float *amax_out,
+                           void *ws, void *stream)
+{
+    if (!ring) return fail(QL_ERR_NULL, "quantize_ring: ring is required");
+    if (hist_len < 1 || hist_len > RING_MAX_HIST)
+        return fail(QL_ERR_VALUE, "quantize_ring: hist_len %lld outside [1, %lld]", (long long)hist_len,
+                    (long long)RING_MAX_HIST);
+    if (idx < 0 || idx >= hist_len)
+        return fail(QL_ERR_VALUE, "quantize_ring: idx %lld outside [0, hist_len)", (long long)idx);
+    if (margin < -RING_MAX_MARGIN || margin > RING_MAX_MARGIN)
+        return fail(QL_ERR_VALUE, "quantize_ring: margin %d outside [-%d, %d]", margin, RING_MAX_MARGIN,
+                    RING_MAX_MARGIN);
+    const float *scale_in = ring + hist_len;
+    ql_status st = check_quantize(x, x_dt, rows, cols, ldx, QL_PER_TENSOR, fmt, scale_in, x_q, ldq, nullptr, ws);
+    if (st != QL_OK) return st;
+    ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, QL_PER_TENSOR, fmt, scale_in, x_q, ldq, nullptr, amax_out,
+                             ql::ws_slot(ws, ql::WS_SLOT_QA));
+    p.ring = ring;
+    p.hist_len = hist_len;
+    p.ring_idx = idx;
+    p.margin = margin;
+    p.scale_used = scale_used;
+    return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize_ring launch");
 }
 
 ql_status ql_qgemm(const void *a_q, ql_qfmt a_fmt, ql_layout a_lay, int64_t lda,

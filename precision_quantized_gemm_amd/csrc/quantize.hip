@@ -126,6 +126,28 @@ __device__ __forceinline__ void publish(const QzParams &p, uint32_t bits, int64_
     if (p.scale_out) p.scale_out[i] = amax / p.qmax;      // IEEE division
 }
 
+// Finalize an amax history ring from the last workgroup (every thread of it
+// calls this): hist[idx] = amax (floored), scale_used = the scale the cast
+// used, ring scale = fl32(max(hist) / qmax) * 2^margin.  History values are
+// non-negative floats, so their maximum is taken on the bit patterns.
+__device__ __forceinline__ void ring_publish(const QzParams &p, uint32_t bits, uint32_t *red)
+{
+    const float a = __uint_as_float(bits);
+    const float amax = a < p.floor ? p.floor : a;
+    uint32_t m = absbits_f32(amax);
+    for (int64_t i = threadIdx.x; i < p.hist_len; i += blockDim.x)
+        if (i != p.ring_idx) { const uint32_t t = absbits_f32(p.ring[i]); m = t > m ? t : m; }
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) {
+        const float used = p.ring[p.hist_len];
+        p.ring[p.ring_idx] = amax;
+        if (p.scale_used) p.scale_used[0] = used;
+        if (p.amax_out) p.amax_out[0] = amax;
+        const float step = __uint_as_float(m) / p.qmax;           // IEEE division
+        p.ring[p.hist_len] = __builtin_ldexpf(step, p.margin);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1 of per-tensor current scaling.
 template <typename T, int MODE>
@@ -233,10 +255,19 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
     }
     if (MEASURE) {
         __shared__ uint32_t red[QZ_THREADS / 64];
+        __shared__ uint32_t last_bits;
+        __shared__ int is_last;
         m = block_max_u32(m, red);
         if (threadIdx.x == 0) {
-            uint32_t bits;
-            if (elect_last_max(p.ws, m, &bits)) publish(p, bits, 0);
+            uint32_t bits = 0;
+            const bool last = elect_last_max(p.ws, m, &bits);
+            if (last && !p.ring) publish(p, bits, 0);
+            is_last = last;
+            last_bits = bits;
+        }
+        if (p.ring) {
+            __syncthreads();
+            if (is_last) ring_publish(p, last_bits, red);   // block-uniform branch
         }
     }
 }

@@ -24,8 +24,8 @@ def _declared():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_qgemm",
-                                  "ql_linear_forward", "ql_status_string", "ql_last_error"])
+    assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring",
+                                  "ql_qgemm", "ql_linear_forward", "ql_status_string", "ql_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -76,6 +76,34 @@ def _quant(**kw):
 ])
 def test_quantize_validation(kw, status):
     assert _quant(**kw) == status
+    assert q.ql_last_error()
+
+
+def _ring(**kw):
+    a = dict(x=P, x_dt=0, rows=4, cols=32, ldx=32, fmt=0, ring=P, hist_len=16, idx=3, margin=0, x_q=Q, ldq=32,
+             scale_used=P, amax_out=P, ws=P, stream=None)
+    a.update(kw)
+    return _st("ql_quantize_ring", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ring=None), _lib.QL_ERR_NULL),
+    (dict(hist_len=0), _lib.QL_ERR_VALUE),
+    (dict(hist_len=(1 << 20) + 1), _lib.QL_ERR_VALUE),
+    (dict(idx=16), _lib.QL_ERR_VALUE),
+    (dict(idx=-1), _lib.QL_ERR_VALUE),
+    (dict(margin=65), _lib.QL_ERR_VALUE),
+    (dict(margin=-65), _lib.QL_ERR_VALUE),
+    (dict(ws=None), _lib.QL_ERR_NULL),
+    (dict(x_dt=1, fmt=4), _lib.QL_ERR_VALUE),
+    (dict(x_dt=2), _lib.QL_ERR_DTYPE),
+    (dict(ldq=8), _lib.QL_ERR_SHAPE),
+    (dict(x_q=None), _lib.QL_ERR_NULL),
+])
+def test_quantize_ring_validation(kw, status):
+    """Every rejected ring call fails before anything is enqueued (no GPU is
+    touched: the pointers are never dereferenced)."""
+    assert _ring(**kw) == status
     assert q.ql_last_error()
 
 

@@ -154,3 +154,38 @@ def test_large_fp8_every_code(orc):
     d = synth.workload("large_fp8")
     for role in ("a", "b"):
         check(orc, d[role], 0, 0, what=f"large_fp8.{role}")
+
+
+@pytest.mark.parametrize("shape,dt,fmt,hist_len", [
+    ((1000, 777), "bf16", 0, 4),        # ragged, scalar path
+    ((2048, 1024), "bf16", 1, 16),      # flat vector path
+    ((513, 2048), "fp32", 2, 3),        # rows path, FP32, INT8
+    ((0, 64), "bf16", 0, 2),            # empty: amax is the floor
+])
+def test_quantize_ring_sequence(orc, shape, dt, fmt, hist_len):
+    """Six delayed-scaling steps through one amax history ring: every step's
+    codes, the scale they used, amax and the whole ring after the step must
+    equal the oracle's bit for bit.  The inputs' spread changes from step to
+    step (including a step much smaller than the window's maximum and a
+    negative and a positive margin), so the published scale both rises and
+    falls as entries leave the window."""
+    rows, cols = shape
+    ring_ref = np.zeros(hist_len + 1, np.float32)
+    ring_ref[-1] = 1.0
+    ring = torch.from_numpy(ring_ref.copy()).cuda()
+    ws = q.new_workspace(torch.device("cuda"))
+    stds = [1.0, 40.0, 0.01, 3.0, 0.5, 1e-3]
+    margins = [0, 0, 1, -2, 0, 3]
+    for t, (std, margin) in enumerate(zip(stds, margins)):
+        idx = t % hist_len
+        if dt == "bf16":
+            x_cpu = synth.random_bf16(71, t, rows, cols, std)
+        else:
+            x_cpu = synth.random_fp32(71, t, rows, cols, std)
+        xq, su, am = q.quantize_ring(x_cpu.cuda(), FMT[fmt], ring, idx, margin, ws=ws)
+        torch.cuda.synchronize()
+        codes, su_ref, am_ref = orc.quantize_ring(_oracle_input(x_cpu), fmt, ring_ref, idx, margin)
+        _same_codes(xq.cpu().numpy(), codes, f"ring step {t}")
+        assert su.item() == su_ref and am.item() == am_ref, (t, su.item(), su_ref, am.item(), am_ref)
+        got_ring = ring.cpu().numpy()
+        assert np.array_equal(got_ring.view(np.uint32), ring_ref.view(np.uint32)), (t, got_ring, ring_ref)
