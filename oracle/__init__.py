@@ -288,3 +288,57 @@ def linear_forward(x, w, bias, fmt, sx_in=None, sw_in=None, ms=None, ns=None):
     return dict(x_q=xq, sx=sx, amax_x=ax, w_q=wq, sw=sw, amax_w=aw,
                 acc=acc, S=sabs, iacc=iacc, H=hb, v=v, ms=np.asarray(ms), ns=np.asarray(ns),
                 sx_used=sx_used, sw_used=sw_used)
+
+
+def linear_backward(g, x_q, x_fmt, sx, w_q, w_fmt, sw, g_fmt=E5M2, sg_in=None, dx_entries=None,
+                    dw_entries=None):
+    """Backward of the quantized linear layer, from the forward's codes.
+
+    Follows the ``linear_backward_fp8`` docstring (AstrAI ops/fp8.py): the
+    output gradient g [M, N] is quantized once, per tensor, to ``g_fmt``
+    (E5M2 by default), and both products run on codes:
+        dX[m, k] = sum_n g[m, n] W[n, k] * sg * sw      ([M, K])
+        dW[n, k] = sum_m g[m, n] X[m, k] * sg * sx      ([N, K])
+    with x_q [M, K] and w_q [N, K] the forward's codes (the reading of the
+    backward workload: E5M2 gradient times the E4M3 forward operands).
+    grad_bias[n] = sum_m g[m, n], the column sum of the unquantized gradient
+    (math.fsum: exact, then rounded once).  dX and dW are evaluated at the
+    listed (m, k) / (n, k) entries (all when None).  Returns a dict with the
+    codes, scale and amax of g and, per product, acc / S / H / v.
+    """
+    import math
+
+    gq, sg, ag = quantize(g, PER_TENSOR, g_fmt, sg_in)
+    sg_used = sg if sg_in is None else np.asarray(sg_in, dtype=np.float32)
+    M, N = gq.shape
+    K = x_q.shape[1]
+
+    def entries(e, rows, cols):
+        if e is not None:
+            return np.asarray(e[0], np.int64), np.asarray(e[1], np.int64)
+        mm, nn = np.meshgrid(np.arange(rows), np.arange(cols), indexing="ij")
+        return mm.ravel().astype(np.int64), nn.ravel().astype(np.int64)
+
+    out = dict(g_q=gq, sg=sg, amax_g=ag, sg_used=sg_used)
+    # dX: A = g codes [M, N] K-major (contraction n); B[k, n] = W[n, k], i.e.
+    # w_q [N, K] read MN-major.
+    ms, ks = entries(dx_entries, M, K)
+    acc, S, _, H = qgemm_entries(gq, g_fmt, K_MAJOR, w_q, w_fmt, MN_MAJOR, N, ms, ks)
+    out["dx"] = dict(ms=ms, ns=ks, acc=acc, S=S, H=H,
+                     v=epilogue(acc, ms, ks, sg_used, PER_TENSOR, np.asarray(sw, np.float32), PER_TENSOR))
+    # dW: A[n, m] = g[m, n] (g codes read MN-major); B[k, m] = X[m, k]
+    # (x_q [M, K] read MN-major); contraction over m.
+    ns, ks = entries(dw_entries, N, K)
+    acc, S, _, H = qgemm_entries(gq, g_fmt, MN_MAJOR, x_q, x_fmt, MN_MAJOR, M, ns, ks)
+    out["dw"] = dict(ms=ns, ns=ks, acc=acc, S=S, H=H,
+                     v=epilogue(acc, ns, ks, sg_used, PER_TENSOR, np.asarray(sx, np.float32), PER_TENSOR))
+    gv = _input_values(g)
+    out["dbias"] = np.array([math.fsum(gv[:, n].tolist()) for n in range(N)], dtype=np.float64)
+    return out
+
+
+def _input_values(x: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) or float32 as float64 values."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)

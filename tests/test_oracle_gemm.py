@@ -177,3 +177,21 @@ def test_truncation_bound_H(orc):
     a2 = a.copy(); a2[0, 0] = 0
     _, _, _, H4 = orc.qgemm_entries(a2, 1, 0, b, 1, 0, 16, [0], [0])
     assert H4[0] == 0.0
+
+
+def test_backward_handworked(orc):
+    """dX = g @ W, dW = g^T @ X and grad_bias on the forward's codes, with
+    one E5M2 quantization of g (tests/golden/backward_handworked.txt)."""
+    gold = {r[0]: r[1:] for r in read_golden("backward_handworked.txt")}
+    g = np.array([float(v) for v in gold["g"]], np.float32).reshape(2, 2)
+    gb = synth.bf16_bits(torch.from_numpy(g).to(torch.bfloat16))
+    xq = np.array([int(c, 16) for c in gold["x_codes"]], np.uint8).reshape(2, 3)
+    wq = np.array([int(c, 16) for c in gold["w_codes"]], np.uint8).reshape(2, 3)
+    r = orc.linear_backward(gb, xq, orc.E4M3, float(gold["sx"][0]), wq, orc.E4M3, float(gold["sw"][0]),
+                            g_fmt=orc.E5M2, sg_in=[1.0])
+    assert list(r["g_q"].ravel()) == [int(c, 16) for c in gold["g_codes_e5m2"]]
+    assert np.array_equal(r["dx"]["v"], np.array([float(v) for v in gold["dx"]]))
+    assert np.array_equal(r["dw"]["v"], np.array([float(v) for v in gold["dw"]]))
+    assert np.array_equal(r["dbias"], np.array([float(v) for v in gold["dbias"]]))
+    # every intermediate is exact here: the truncation bound is 0
+    assert not r["dx"]["H"].any() and not r["dw"]["H"].any()
