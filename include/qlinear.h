@@ -236,6 +236,45 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                             void *w_q, float *sw, float *amax_w,
                             void *ws, void *stream);
 
+/* ------------------------------------------------------------------------
+ * ql_linear_backward -- backward of the quantized linear layer.
+ *
+ * [FP8PY] linear_backward_fp8 docstring: the output gradient is quantized
+ * once (E5M2 by default, the wider range) and that quantization is shared
+ * by the two matrix-core products; grad_bias comes back beside them and
+ * `masks` selects which results are produced.  The products take the
+ * forward's codes (the backward workload pairs an E5M2 gradient with the
+ * E4M3 forward operands) in their stored layouts, with no transposed
+ * copies:
+ *   dX [M, K] = (g_q . W) * sg * sw   (W read MN-major from w_q [N, K])
+ *   dW [N, K] = (g_q^T . X) * sg * sx (g_q and x_q [M, K] read MN-major)
+ *   dbias [N] = column sums of the BF16 g (FP32, fixed summation order)
+ *
+ *   g        BF16 [M, N] row-major (leading dimension N).
+ *   x_q, sx  forward codes of x [M, K] (leading dimension K) and their
+ *            per-tensor step [1]; w_q, sw the same for w [N, K].
+ *   masks    non-empty OR of QL_BWD_DX, QL_BWD_DW, QL_BWD_DBIAS.
+ *   g_fmt    E4M3 or E5M2 (x_fmt / w_fmt likewise; INT8 is not a backward
+ *            format).  sg_in: NULL = current scaling (sg = amax/qmax of
+ *            g), else the delayed step [1] the codes use.
+ *   dx, dw   outputs ([M, K], [N, K], leading dimension K) in out_dt (BF16
+ *            or FP32); required when their mask bit is set.
+ *   dbias    FP32 [N], required with QL_BWD_DBIAS.
+ *   g_q, sg, amax_g  g's codes [M, N] and its per-tensor step and amax, as
+ *            ql_quantize writes them; required when dX or dW is produced.
+ *   ws       workspace (required when dX or dW is produced).
+ * Errors: as ql_quantize and ql_qgemm, plus QL_ERR_VALUE for a bad mask.
+ * ---------------------------------------------------------------------- */
+#define QL_BWD_DX 1u
+#define QL_BWD_DW 2u
+#define QL_BWD_DBIAS 4u
+ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
+                             const void *x_q, ql_qfmt x_fmt, const float *sx,
+                             const void *w_q, ql_qfmt w_fmt, const float *sw, int64_t K,
+                             unsigned masks, ql_qfmt g_fmt, const float *sg_in,
+                             void *dx, void *dw, ql_dtype out_dt, float *dbias,
+                             void *g_q, float *sg, float *amax_g, void *ws, void *stream);
+
 /* Short fixed text for a status code (never NULL). */
 const char *ql_status_string(ql_status s);
 

@@ -216,3 +216,49 @@ def linear_forward(x, w, bias=None, fmt="e4m3", *, sx_in=None, sw_in=None, out_d
                            _ptr(r.out_amax), r.x_q.data_ptr(), r.sx.data_ptr(), r.amax_x.data_ptr(),
                            r.w_q.data_ptr(), r.sw.data_ptr(), r.amax_w.data_ptr(), ws.data_ptr(), _stream())
     return r
+
+
+@dataclass
+class LinearGrads:
+    dx: Optional[torch.Tensor]
+    dw: Optional[torch.Tensor]
+    dbias: Optional[torch.Tensor]
+    g_q: Optional[torch.Tensor]
+    sg: Optional[torch.Tensor]
+    amax_g: Optional[torch.Tensor]
+
+
+def linear_backward(g, x_q, sx, w_q, sw, *, x_fmt="e4m3", w_fmt="e4m3", g_fmt="e5m2",
+                    masks=(True, True, True), sg_in=None, out_dtype="bf16", ws=None) -> LinearGrads:
+    """Backward of the quantized linear layer from the forward's codes.
+
+    ``g`` is the BF16 output gradient [M, N]; ``x_q`` [M, K] / ``w_q`` [N, K]
+    and their steps ``sx`` / ``sw`` come from the forward.  ``masks`` picks
+    (dX, dW, grad_bias).  g is quantized once to ``g_fmt`` for both products.
+    """
+    if g.dtype != torch.bfloat16:
+        raise TypeError(f"linear_backward requires a bf16 gradient, got {g.dtype}")
+    M, N = g.shape
+    K = x_q.shape[1]
+    dev = g.device
+    want_dx, want_dw, want_db = (bool(m) for m in masks)
+    bits = (_lib.QL_BWD_DX if want_dx else 0) | (_lib.QL_BWD_DW if want_dw else 0) | \
+        (_lib.QL_BWD_DBIAS if want_db else 0)
+    if out_dtype not in ("bf16", "fp32"):
+        raise ValueError("linear_backward writes bf16 or fp32 gradients")
+    odt, tdt = _OUT_DT[out_dtype]
+    gemms = want_dx or want_dw
+    dx = torch.empty((M, K), dtype=tdt, device=dev) if want_dx else None
+    dw = torch.empty((N, K), dtype=tdt, device=dev) if want_dw else None
+    dbias = torch.empty(N, dtype=torch.float32, device=dev) if want_db else None
+    g_q = torch.empty((M, N), dtype=torch.uint8, device=dev) if gemms else None
+    sg = torch.empty(1, dtype=torch.float32, device=dev) if gemms else None
+    amax_g = torch.empty(1, dtype=torch.float32, device=dev) if gemms else None
+    if ws is None and gemms:
+        ws = workspace(dev)
+    g = g.contiguous()
+    _lib.ql_linear_backward(g.data_ptr(), M, N, x_q.data_ptr(), _enum(FMTS, x_fmt, "format"), sx.data_ptr(),
+                            w_q.data_ptr(), _enum(FMTS, w_fmt, "format"), sw.data_ptr(), K, bits,
+                            _enum(FMTS, g_fmt, "format"), _ptr(sg_in), _ptr(dx), _ptr(dw), odt, _ptr(dbias),
+                            _ptr(g_q), _ptr(sg), _ptr(amax_g), _ptr(ws), _stream())
+    return LinearGrads(dx, dw, dbias, g_q, sg, amax_g)

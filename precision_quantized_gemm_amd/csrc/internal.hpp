@@ -47,6 +47,8 @@ struct QzParams {
 };
 
 hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s);
+// grad_bias: out[n] = sum_m g[m, n] for BF16 g [M, N] (leading dimension ldg).
+hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, hipStream_t s);
 hipError_t launch_ws_zero(void *ws, int64_t bytes, hipStream_t s);
 
 struct GemmParams {

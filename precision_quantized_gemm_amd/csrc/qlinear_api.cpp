@@ -330,6 +330,74 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
     return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
 }
 
+ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
+                             const void *x_q, ql_qfmt x_fmt, const float *sx,
+                             const void *w_q, ql_qfmt w_fmt, const float *sw, int64_t K,
+                             unsigned masks, ql_qfmt g_fmt, const float *sg_in,
+                             void *dx, void *dw, ql_dtype out_dt, float *dbias,
+                             void *g_q, float *sg, float *amax_g, void *ws, void *stream)
+{
+    if (masks == 0 || (masks & ~7u))
+        return fail(QL_ERR_VALUE, "linear_backward: masks %u must be a non-empty subset of 1|2|4", masks);
+    const bool want_dx = masks & QL_BWD_DX, want_dw = masks & QL_BWD_DW, want_db = masks & QL_BWD_DBIAS;
+    if (out_dt != QL_DT_BF16 && out_dt != QL_DT_FP32)
+        return fail(valid_dtype(out_dt) ? QL_ERR_DTYPE : QL_ERR_VALUE,
+                    "linear_backward: gradients are BF16 or FP32, got dtype %d", out_dt);
+    if (g_fmt == QL_FMT_INT8 || x_fmt == QL_FMT_INT8 || w_fmt == QL_FMT_INT8)
+        return fail(valid_fmt(g_fmt) && valid_fmt(x_fmt) && valid_fmt(w_fmt) ? QL_ERR_DTYPE : QL_ERR_VALUE,
+                    "linear_backward: FP8 formats only");
+    if (K < 0) return fail(QL_ERR_VALUE, "linear_backward: negative K");
+    ql_status st;
+    if (want_db) {
+        if (M < 0 || N < 0) return fail(QL_ERR_VALUE, "linear_backward: negative size");
+        if (!dbias && N > 0) return fail(QL_ERR_NULL, "linear_backward: dbias is required by the mask");
+        if (!g && M > 0 && N > 0) return fail(QL_ERR_NULL, "linear_backward: g is required");
+    }
+    const bool gemms = want_dx || want_dw;
+    GemmArgs gx{}, gw{};
+    if (gemms) {
+        if (!sg || !amax_g) return fail(QL_ERR_NULL, "linear_backward: sg and amax_g are required outputs");
+        st = check_quantize(g, QL_DT_BF16, M, N, N, QL_PER_TENSOR, g_fmt, sg_in, g_q, N, sg, ws);
+        if (st != QL_OK) return st;
+        const float *sg_use = sg_in ? sg_in : sg;
+        // dX [M, K] = g [M, N] . W: A = g codes (K-major over n), B[k, n] =
+        // W[n, k] read MN-major from w_q [N, K].
+        gx = GemmArgs{g_q, g_fmt, QL_K_MAJOR, N, w_q, w_fmt, QL_MN_MAJOR, K, M, K, N,
+                      sg_use, QL_PER_TENSOR, sw, QL_PER_TENSOR, nullptr, QL_DT_FP32, dx, out_dt, K,
+                      nullptr, nullptr, ws};
+        // dW [N, K] = g^T . X: A[n, m] = g[m, n] read MN-major from the g
+        // codes, B[k, m] = X[m, k] read MN-major from x_q [M, K].
+        gw = GemmArgs{g_q, g_fmt, QL_MN_MAJOR, N, x_q, x_fmt, QL_MN_MAJOR, K, N, K, M,
+                      sg_use, QL_PER_TENSOR, sx, QL_PER_TENSOR, nullptr, QL_DT_FP32, dw, out_dt, K,
+                      nullptr, nullptr, ws};
+        if (want_dx && (st = check_gemm(gx)) != QL_OK) return st;
+        if (want_dw && (st = check_gemm(gw)) != QL_OK) return st;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gemms) {
+        ql::QzParams pg = make_qz(g, QL_DT_BF16, M, N, N, QL_PER_TENSOR, g_fmt, sg_in, g_q, N, sg, amax_g,
+                                  ql::ws_slot(ws, ql::WS_SLOT_QA));
+        hipError_t e = ql::launch_quantize(pg, QL_DT_BF16, g_fmt, s);
+        if (e != hipSuccess) return hip_status(e, "linear_backward: quantize g");
+        if (want_dx) {
+            ql::GemmParams p = make_gemm(gx, nullptr);
+            e = ql::launch_qgemm(p, g_fmt, w_fmt, 0, 1, s);
+            if (e != hipSuccess) return hip_status(e, "linear_backward: dX");
+        }
+        if (want_dw) {
+            ql::GemmParams p = make_gemm(gw, nullptr);
+            e = ql::launch_qgemm(p, g_fmt, x_fmt, 1, 1, s);
+            if (e != hipSuccess) return hip_status(e, "linear_backward: dW");
+        }
+    }
+    if (want_db && M >= 0 && N > 0) {
+        hipError_t e = ql::launch_col_sum_bf16(g, M, N, N, dbias, s);
+        if (e != hipSuccess) return hip_status(e, "linear_backward: grad_bias");
+    }
+    return QL_OK;
+}
+
 const char *ql_status_string(ql_status s)
 {
     switch (s) {

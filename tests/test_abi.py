@@ -25,7 +25,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring",
-                                  "ql_qgemm", "ql_linear_forward", "ql_status_string", "ql_last_error"])
+                                  "ql_qgemm", "ql_linear_forward", "ql_linear_backward", "ql_status_string",
+                                  "ql_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -174,3 +175,31 @@ def test_python_errors_map_to_exceptions():
         q.ql_quantize(P, 2, 4, 32, 32, 0, 0, None, Q, 32, P, P, P)
     with pytest.raises(q.QLError):
         q.ql_quantize(None, 0, 4, 32, 32, 0, 0, None, Q, 32, P, P, P)
+
+
+def _bwd(**kw):
+    a = dict(g=P, M=64, N=32, x_q=Q, x_fmt=0, sx=P, w_q=Q, w_fmt=0, sw=P, K=48, masks=7, g_fmt=1, sg_in=None,
+             dx=Q, dw=Q, out_dt=0, dbias=P, g_q=Q, sg=P, amax_g=P, ws=P, stream=None)
+    a.update(kw)
+    return _st("ql_linear_backward", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(masks=0), _lib.QL_ERR_VALUE),
+    (dict(masks=8), _lib.QL_ERR_VALUE),
+    (dict(out_dt=2), _lib.QL_ERR_DTYPE),          # gradients are BF16 / FP32
+    (dict(out_dt=9), _lib.QL_ERR_VALUE),
+    (dict(g_fmt=2), _lib.QL_ERR_DTYPE),           # INT8 is not a backward format
+    (dict(x_fmt=5), _lib.QL_ERR_VALUE),
+    (dict(K=-1), _lib.QL_ERR_VALUE),
+    (dict(masks=4, dbias=None), _lib.QL_ERR_NULL),
+    (dict(sg=None), _lib.QL_ERR_NULL),
+    (dict(g_q=None), _lib.QL_ERR_NULL),
+    (dict(ws=None), _lib.QL_ERR_NULL),
+    (dict(masks=1, dx=None), _lib.QL_ERR_NULL),
+    (dict(masks=2, dw=None), _lib.QL_ERR_NULL),
+    (dict(masks=1, w_q=None), _lib.QL_ERR_NULL),
+])
+def test_linear_backward_validation(kw, status):
+    assert _bwd(**kw) == status
+    assert q.ql_last_error()

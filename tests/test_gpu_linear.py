@@ -73,3 +73,80 @@ def test_linear_forward_delayed_fp8_out_and_int8(orc):
     _compare_quant(r8, ref8)
     got = r8.out.cpu().numpy().astype(np.float64).ravel()
     assert np.all(np.abs(got - ref8["v"]) <= 3 * 2.0 ** -24 * np.abs(ref8["v"]))
+
+
+def _dbias_bound(g_vals, M):
+    """FP32 column sums in a fixed order of M/16 + 16 additions."""
+    n = M // 16 + 17
+    u = 2.0 ** -24
+    return (n * u / (1 - n * u)) * np.abs(g_vals).sum(axis=0) + 1e-45
+
+
+def _backward_case(orc, g, x_q, sx, w_q, sw, masks, sg_in=None, out_dtype="bf16", g_fmt=1, rows=4, cols=4,
+                   rand=2048, what=""):
+    dev = "cuda"
+    M, N = g.shape
+    K = x_q.shape[1]
+    r = q.linear_backward(g.to(dev), torch.from_numpy(x_q).to(dev), torch.tensor([sx], device=dev),
+                          torch.from_numpy(w_q).to(dev), torch.tensor([sw], device=dev),
+                          g_fmt={0: "e4m3", 1: "e5m2"}[g_fmt], masks=masks,
+                          sg_in=None if sg_in is None else torch.tensor([sg_in], device=dev), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M * 7 + N)
+    def sample(R, C):
+        rr = rng.choice(R, min(rows, R), replace=False)
+        cc = rng.choice(C, min(cols, C), replace=False)
+        ms = np.concatenate([np.repeat(rr, C), np.tile(np.arange(R), len(cc)), rng.integers(0, R, rand)])
+        ns = np.concatenate([np.tile(np.arange(C), len(rr)), np.repeat(cc, R), rng.integers(0, C, rand)])
+        return ms.astype(np.int64), ns.astype(np.int64)
+    dxe, dwe = sample(M, K), sample(N, K)
+    ref = orc.linear_backward(_bits(g), x_q, 0, np.float32(sx), w_q, 0, np.float32(sw), g_fmt=g_fmt,
+                              sg_in=None if sg_in is None else [sg_in], dx_entries=dxe, dw_entries=dwe)
+    if masks[0] or masks[1]:
+        assert np.array_equal(r.g_q.cpu().numpy(), ref["g_q"]), what
+        assert r.sg.cpu().numpy().view(np.uint32)[0] == ref["sg"].view(np.uint32)[0], what
+        assert r.amax_g.cpu().numpy().view(np.uint32)[0] == ref["amax_g"].view(np.uint32)[0], what
+    sg_used = float(ref["sg_used"][0])
+    conv = (lambda t: t.to(torch.float64).numpy()) if out_dtype == "bf16" else (lambda t: t.numpy().astype(np.float64))
+    if masks[0]:
+        e = ref["dx"]
+        got = conv(r.dx.cpu())[e["ms"], e["ns"]]
+        print(what, "dX", check_float(got, e["v"], e["S"], e["H"], sg_used * np.float32(sw), N, what=what + " dX"))
+    else:
+        assert r.dx is None
+    if masks[1]:
+        e = ref["dw"]
+        got = conv(r.dw.cpu())[e["ms"], e["ns"]]
+        print(what, "dW", check_float(got, e["v"], e["S"], e["H"], sg_used * np.float32(sx), M, what=what + " dW"))
+    else:
+        assert r.dw is None
+    if masks[2]:
+        gv = g.float().numpy().astype(np.float64)
+        err = np.abs(r.dbias.cpu().numpy().astype(np.float64) - ref["dbias"])
+        assert np.all(err <= _dbias_bound(gv, M)), (what, err.max())
+
+
+def test_linear_backward_workload(orc):
+    """The backward workload at full size: G BF16 [2048, 4096] ~ N(0, 1e-3)
+    quantized to E5M2 once for dX = G . W (W read MN-major) and dW = G^T . X
+    (both MN-major), with x_q and w_q the E4M3 forward codes of the MLP-up
+    layer; plus grad_bias.  Codes, scale and amax of G bit for bit; dX and dW
+    on sampled entries within the float bound; grad_bias within the FP32
+    summation bound."""
+    d = synth.workload("mlp_backward")
+    x_q, sx, _ = orc.quantize(_bits(d["x"]), 0, 0)
+    w_q, sw, _ = orc.quantize(_bits(d["w"]), 0, 0)
+    _backward_case(orc, d["g"], x_q, float(sx[0]), w_q, float(sw[0]), (True, True, True), what="mlp_backward")
+
+
+@pytest.mark.parametrize("masks", [(True, False, False), (False, True, False), (False, False, True),
+                                   (True, True, True)])
+def test_linear_backward_ragged_masks(orc, masks):
+    """Ragged shapes (partial tiles on every side) for each output selection,
+    FP32 gradients, and a delayed gradient step."""
+    M, N, K = 333, 517, 259
+    g = synth.random_bf16(81, 0, M, N, 0.03)
+    x_q, sx, _ = orc.quantize(synth.bf16_bits(synth.random_bf16(81, 1, M, K)), 0, 0)
+    w_q, sw, _ = orc.quantize(synth.bf16_bits(synth.random_bf16(81, 2, N, K, 0.05)), 0, 0)
+    _backward_case(orc, g, x_q, float(sx[0]), w_q, float(sw[0]), masks, sg_in=2.0 ** -12, out_dtype="fp32",
+                   what=f"ragged {masks}")
