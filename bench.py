@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--cpu-rows", type=int, default=64, help="output rows in the oracle GEMM sample")
     ap.add_argument("--cpu-cols", type=int, default=4096, help="output columns in the oracle GEMM sample")
     return ap.parse_args()
@@ -117,6 +118,27 @@ def cpu_baseline(a_cpu, b_cpu, M, N, K, rows, cols):
                         f"({ms.size * K} MACs, {threads} threads, {tg_wall:.1f} s); scaled to the full "
                         f"{M}x{N}x{K} step"),
                 step_seconds_estimate=step_s)
+
+
+def time_backward(torch, q, synth, dev, reps):
+    """ms per ql_linear_backward call on the MLP-up layer's backward and the
+    rate of its two products (2 x 2*M*N*K flops)."""
+    d = synth.workload("mlp_backward")
+    g = d["g"].to(dev)
+    fx = q.quantize(d["x"].to(dev), "per_tensor", "e4m3")
+    fw = q.quantize(d["w"].to(dev), "per_tensor", "e4m3")
+    ws = q.new_workspace(dev)
+    run = lambda: q.linear_backward(g, fx[0], fx[1], fw[0], fw[1], ws=ws)
+    for _ in range(3):
+        run()
+    ms = time_events(run, reps, torch)
+    M, N = g.shape
+    K = fx[0].shape[1]
+    flops = 2 * 2.0 * M * N * K
+    return {"workload": f"g BF16 [{M},{N}] N(0,1e-3) -> E5M2; x_q [{M},{K}], w_q [{N},{K}] E4M3; dX, dW (BF16), "
+                        "grad_bias in one ql_linear_backward",
+            "ms_per_call": round(ms, 5), "gemm_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
 
 
 def kernel_source_hash():
@@ -271,6 +293,14 @@ def main():
     torch.cuda.synchronize()
     ms_ring = e0.elapsed_time(e1) / args.steps
 
+    # Backward of the MLP-up layer (G [2048, 4096] BF16 -> E5M2, x_q
+    # [2048, 1024] and w_q [4096, 1024] E4M3): one ql_linear_backward call
+    # (quantize G, dX = G.W, dW = G^T.X with MN-major operands, grad_bias).
+    bwd = None
+    if not args.no_backward:
+        log("backward")
+        bwd = time_backward(torch, q, synth, dev, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -319,6 +349,7 @@ def main():
             "a_ring_note": "ql_quantize_ring (delayed scaling, 16-entry history), back to back on a",
             "peak_GBps": PEAK_HBM_GBPS,
         },
+        "linear_backward": bwd,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
         "wall_s_timed_region": round(t_wall, 4),

@@ -85,6 +85,8 @@ def _load():
     lib.orc_qgemm_entries.restype = None
     lib.orc_epilogue.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp]
     lib.orc_epilogue.restype = None
+    lib.orc_qbias_values.argtypes = [vp, i64, i32, flt, vp]
+    lib.orc_qbias_values.restype = None
     lib.orc_fp8_output.argtypes = [vp, i64, flt, i32, vp]
     lib.orc_fp8_output.restype = None
     _lib = lib
@@ -235,7 +237,8 @@ def qgemm_full(a, a_fmt, a_lay, b, b_fmt, b_lay, M, N, K):
 
 
 def epilogue(acc, ms, ns, sa, sa_gran, sb, sb_gran, bias=None):
-    """v = acc * sa * sb + bias in double, per entry."""
+    """v = acc * sa * sb + bias in double, per entry.  ``bias`` is BF16 bits
+    (uint16), float32, or float64 values (a decoded quantized bias)."""
     acc = np.ascontiguousarray(acc, dtype=np.float64)
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)
@@ -243,7 +246,10 @@ def epilogue(acc, ms, ns, sa, sa_gran, sb, sb_gran, bias=None):
     sb = np.ascontiguousarray(sb, dtype=np.float32)
     out = np.zeros(acc.size, dtype=np.float64)
     bptr, bdt = None, 0
-    if bias is not None:
+    if bias is not None and np.asarray(bias).dtype == np.float64:
+        bias, bdt = np.ascontiguousarray(bias, dtype=np.float64), 2
+        bptr = _ptr(bias)
+    elif bias is not None:
         bias, bdt = _input_view(np.asarray(bias).reshape(1, -1))
         bptr = _ptr(bias)
     _load().orc_epilogue(_ptr(acc), _ptr(ms), _ptr(ns), acc.size, _ptr(sa), sa_gran,
@@ -342,3 +348,30 @@ def _input_values(x: np.ndarray) -> np.ndarray:
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def qbias_values(codes: np.ndarray, fmt: int, bias_scale: float) -> np.ndarray:
+    """Values of a quantized bias: dec(code) * bias_scale, float64."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+    out = np.zeros(c.size, dtype=np.float64)
+    _load().orc_qbias_values(_ptr(c), c.size, fmt, float(np.float32(bias_scale)), _ptr(out))
+    return out
+
+
+def linear_forward_static(x, w_q, w_fmt, sw, bias_q, bias_scale, fmt, sx_in=None, ms=None, ns=None):
+    """Static FP8 inference ([FP8PY] linear_forward_fp8 docstring): w (and
+    optionally the bias) arrive already quantized to ``fmt`` with their steps
+    ``sw`` / ``bias_scale``; only x is quantized.  Returns x's codes, step and
+    amax and, at entries (ms, ns), acc / S / H / v."""
+    xq, sx, ax = quantize(x, PER_TENSOR, fmt, sx_in)
+    M, K = xq.shape
+    N = w_q.shape[0]
+    if ms is None:
+        mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ms, ns = mm.ravel(), nn.ravel()
+    acc, S, _, H = qgemm_entries(xq, fmt, K_MAJOR, w_q, w_fmt, K_MAJOR, K, ms, ns)
+    sx_used = sx if sx_in is None else np.asarray(sx_in, dtype=np.float32)
+    bias = None if bias_q is None else qbias_values(bias_q, fmt, bias_scale)
+    v = epilogue(acc, ms, ns, sx_used, PER_TENSOR, np.asarray(sw, np.float32), PER_TENSOR, bias)
+    return dict(x_q=xq, sx=sx, amax_x=ax, acc=acc, S=S, H=H, v=v, ms=np.asarray(ms), ns=np.asarray(ns),
+                sx_used=sx_used, bias=bias)

@@ -35,7 +35,7 @@
 
 /* Format and dtype numbers used by this file's entry points. */
 enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_INT8 = 2 };
-enum { ORC_IN_BF16 = 0, ORC_IN_FP32 = 1 };
+enum { ORC_IN_BF16 = 0, ORC_IN_FP32 = 1, ORC_BIAS_F64 = 2 };
 enum { ORC_PER_TENSOR = 0, ORC_PER_ROW = 1 };
 enum { ORC_K_MAJOR = 0, ORC_MN_MAJOR = 1 };
 
@@ -376,9 +376,17 @@ void orc_epilogue(const double *acc, const int64_t *ms, const int64_t *ns, int64
     for (int64_t e = 0; e < count; ++e) {
         double v = acc[e] * (double)sa[sa_gran == ORC_PER_ROW ? ms[e] : 0]
                           * (double)sb[sb_gran == ORC_PER_ROW ? ns[e] : 0];
-        if (bias) v += orc_load(bias, bias_dt, ns[e]);
+        if (bias) v += bias_dt == ORC_BIAS_F64 ? ((const double *)bias)[ns[e]] : orc_load(bias, bias_dt, ns[e]);
         v_out[e] = v;
     }
+}
+
+/* Static FP8 inference ([FP8PY] linear_forward_fp8 docstring): the bias may
+ * arrive quantized to the layer's format with its own step bias_scale; its
+ * value is then dec(code) * bias_scale (exact in double).                  */
+void orc_qbias_values(const uint8_t *codes, int64_t n, int fmt, float bias_scale, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_decode(codes[i], fmt) * (double)bias_scale;
 }
 
 /* FP8 output: code = sat(RNE(v / out_scale)) in E4M3.  out_scale is the

@@ -54,6 +54,12 @@ def test_handworked(orc):
     ib = np.array([[int(x) for x in g["int8_b"]]], np.int8).view(np.uint8)
     _, _, iacc, *_ = orc.qgemm_entries(ia, orc.INT8, orc.K_MAJOR, ib, orc.INT8, orc.K_MAJOR, 2, [0], [0])
     assert iacc[0] == int(g["int8_acc"][0])
+    # static inference: the quantized bias decodes to dec(code) * bias_scale
+    qb = orc.qbias_values(np.array([int(g["qbias_code"][0], 16)], np.uint8), orc.E4M3, float(g["bias_scale"][0]))
+    assert qb[0] == float(np.float32(0.1))
+    vq = orc.epilogue(acc, [0], [0], sa, orc.PER_TENSOR, sb, orc.PER_TENSOR, qb)
+    bfq = torch.tensor(vq[0], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    assert bfq == int(g["qbias_bf16_out"][0], 16)
 
 
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
@@ -195,3 +201,14 @@ def test_backward_handworked(orc):
     assert np.array_equal(r["dbias"], np.array([float(v) for v in gold["dbias"]]))
     # every intermediate is exact here: the truncation bound is 0
     assert not r["dx"]["H"].any() and not r["dw"]["H"].any()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_qbias_values_match_decode(orc, fmt):
+    """Every finite code's quantized-bias value is the decoded code times the
+    step, exactly (a power-of-two step keeps every product exact in both)."""
+    codes = np.arange(256, dtype=np.uint8)
+    dec = orc.fp8_decode_array(codes, fmt)
+    ok = np.isfinite(dec)
+    got = orc.qbias_values(codes[ok], fmt, 0.25)
+    assert np.array_equal(got, dec[ok] * 0.25)
