@@ -293,6 +293,17 @@ def main():
     torch.cuda.synchronize()
     ms_ring = e0.elapsed_time(e1) / args.steps
 
+    # Static FP8 inference on the same layer: w arrives quantized (the w_q /
+    # sw the step produced), so a call quantizes a and runs the GEMM.
+    def static_step():
+        q.ql_linear_forward_static(P(a), _lib.QL_DT_BF16, M, K, P(w_q), N, P(sw), None, 0, None,
+                                   _lib.QL_FMT_E4M3, None, P(out), _lib.QL_DT_E4M3, P(out_scale), P(out_amax),
+                                   P(x_q), P(sx), P(amax_x), P(ws), stream)
+
+    for _ in range(3):
+        static_step()
+    ms_static = time_events(static_step, args.steps, torch)
+
     # Backward of the MLP-up layer (G [2048, 4096] BF16 -> E5M2, x_q
     # [2048, 1024] and w_q [4096, 1024] E4M3): one ql_linear_backward call
     # (quantize G, dX = G.W, dW = G^T.X with MN-major operands, grad_bias).
@@ -349,6 +360,9 @@ def main():
             "a_ring_note": "ql_quantize_ring (delayed scaling, 16-entry history), back to back on a",
             "peak_GBps": PEAK_HBM_GBPS,
         },
+        "static_inference": {"ms_per_step": round(ms_static, 5),
+                             "TFLOPs": round(flops / (ms_static * 1e-3) / 1e12, 2),
+                             "workload": "ql_linear_forward_static: quantize a, GEMM with the pre-quantized b"},
         "linear_backward": bwd,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},

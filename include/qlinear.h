@@ -237,6 +237,33 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                             void *ws, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ql_linear_forward_static -- static FP8 inference.
+ *
+ * [FP8PY] linear_forward_fp8 docstring: for static inference the weight
+ * (and optionally the bias) arrive already quantized to the layer's format,
+ * with their steps; a quantized bias needs its own step (bias_scale) and
+ * the weight's amax is not measured.  Only x is quantized here:
+ *   x_q = quantize(x) (per tensor, current or delayed as sx_in says),
+ *   out = (x_q . w_q^T) * sx * sw + bias.
+ *
+ *   x, x_dt, M, K, sx_in, x_q, sx, amax_x, out, out_dt, out_scale, out_amax,
+ *            ws: as ql_linear_forward.
+ *   w_q      [N, K] codes of `fmt` (leading dimension K); sw its step [1].
+ *   fmt      E4M3 or E5M2.
+ *   bias     NULL; or [N] BF16/FP32 values (bias_dt) with bias_scale NULL;
+ *            or, with bias_scale non-NULL ([1]), [N] codes of `fmt` whose
+ *            values are dec(code) * bias_scale (bias_dt is then ignored).
+ * Errors: as ql_linear_forward; QL_ERR_DTYPE for INT8; QL_ERR_NULL without
+ * sw.
+ * ---------------------------------------------------------------------- */
+ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
+                                  const void *w_q, int64_t N, const float *sw,
+                                  const void *bias, ql_dtype bias_dt, const float *bias_scale,
+                                  ql_qfmt fmt, const float *sx_in,
+                                  void *out, ql_dtype out_dt, const float *out_scale, float *out_amax,
+                                  void *x_q, float *sx, float *amax_x, void *ws, void *stream);
+
+/* ------------------------------------------------------------------------
  * ql_linear_backward -- backward of the quantized linear layer.
  *
  * [FP8PY] linear_backward_fp8 docstring: the output gradient is quantized

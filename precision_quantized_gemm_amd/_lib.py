@@ -59,6 +59,9 @@ def load():
     lib.ql_linear_forward.argtypes = [vp, i32, i64, i64, vp, i64, vp, i32, i32, vp, vp,
                                       vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_forward.restype = i32
+    lib.ql_linear_forward_static.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, vp, i32, vp,
+                                             vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.ql_linear_forward_static.restype = i32
     lib.ql_linear_backward.argtypes = [vp, i64, i64, vp, i32, vp, vp, i32, vp, i64, ctypes.c_uint, i32, vp,
                                        vp, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_backward.restype = i32
@@ -114,6 +117,13 @@ def ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out
     _check(load().ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out,
                                     out_dt, out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w,
                                     ws, stream), "ql_linear_forward")
+
+
+def ql_linear_forward_static(x, x_dt, M, K, w_q, N, sw, bias, bias_dt, bias_scale, fmt, sx_in, out, out_dt,
+                             out_scale, out_amax, x_q, sx, amax_x, ws, stream=0) -> None:
+    _check(load().ql_linear_forward_static(x, x_dt, M, K, w_q, N, sw, bias, bias_dt, bias_scale, fmt, sx_in, out,
+                                           out_dt, out_scale, out_amax, x_q, sx, amax_x, ws, stream),
+           "ql_linear_forward_static")
 
 
 QL_BWD_DX, QL_BWD_DW, QL_BWD_DBIAS = 1, 2, 4

@@ -218,6 +218,40 @@ def linear_forward(x, w, bias=None, fmt="e4m3", *, sx_in=None, sw_in=None, out_d
     return r
 
 
+def linear_forward_static(x, w_q, sw, bias=None, bias_scale=None, fmt="e4m3", *, sx_in=None, out_dtype="bf16",
+                          out_scale=None, out_amax=False, ws=None) -> LinearOut:
+    """Static FP8 inference: w arrives quantized (codes ``w_q`` [N, K] of
+    ``fmt`` with step ``sw``); ``bias`` is BF16/FP32 values, or codes of
+    ``fmt`` when ``bias_scale`` is given.  Only x is quantized.  The result's
+    ``w_q``/``sw`` are the inputs and ``amax_w`` is 0 (not measured)."""
+    if x.dtype not in _IN_DT:
+        raise TypeError(f"linear_forward_static requires bf16 or fp32 x, got {x.dtype}")
+    x = x.contiguous()
+    f = _enum(FMTS, fmt, "format")
+    M, K = x.shape
+    N = w_q.shape[0]
+    odt, tdt = _OUT_DT[out_dtype]
+    dev = x.device
+    r = LinearOut(out=torch.empty((M, N), dtype=tdt, device=dev),
+                  x_q=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                  sx=torch.empty(1, dtype=torch.float32, device=dev),
+                  amax_x=torch.empty(1, dtype=torch.float32, device=dev),
+                  w_q=w_q, sw=sw, amax_w=torch.zeros(1, dtype=torch.float32, device=dev),
+                  out_amax=torch.empty(1, dtype=torch.float32, device=dev) if out_amax else None)
+    bias_dt = 0
+    if bias is not None and bias_scale is None:
+        if bias.dtype not in _IN_DT:
+            raise TypeError(f"bias must be bf16 or fp32 values, or codes with bias_scale; got {bias.dtype}")
+        bias_dt = _IN_DT[bias.dtype]
+    if ws is None:
+        ws = workspace(dev)
+    _lib.ql_linear_forward_static(x.data_ptr(), _IN_DT[x.dtype], M, K, w_q.data_ptr(), N, sw.data_ptr(),
+                                  _ptr(bias), bias_dt, _ptr(bias_scale), f, _ptr(sx_in), r.out.data_ptr(), odt,
+                                  _ptr(out_scale), _ptr(r.out_amax), r.x_q.data_ptr(), r.sx.data_ptr(),
+                                  r.amax_x.data_ptr(), ws.data_ptr(), _stream())
+    return r
+
+
 @dataclass
 class LinearGrads:
     dx: Optional[torch.Tensor]

@@ -7,6 +7,10 @@
 
 namespace ql {
 
+// Quantized bias (static inference): codes of the layer's format times a
+// per-tensor step.
+enum : int { BIAS_Q_E4M3 = 16, BIAS_Q_E5M2 = 17 };
+
 // Workspace layout: slots of 256 bytes, each {amax bits, counter, ...}.
 constexpr int64_t WS_SLOT_BYTES = 256;
 constexpr int64_t WS_SLOT_QA = 0;      // quantize of x / A
@@ -58,7 +62,8 @@ struct GemmParams {
     const float *sa, *sb;
     int64_t sa_stride, sb_stride;   // 0 (per tensor) or 1 (per row)
     const void *bias;
-    int bias_dt;                    // -1 none, 0 BF16, 1 FP32
+    int bias_dt;                    // -1 none, 0 BF16, 1 FP32, BIAS_Q_E4M3 / BIAS_Q_E5M2 codes
+    const float *bias_scale;        // step of a quantized bias ([1])
     void *out;
     int64_t ldo;
     int out_dt;                     // DT_BF16 / DT_FP32 / DT_E4M3 / DT_INT32

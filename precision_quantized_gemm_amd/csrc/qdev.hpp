@@ -133,6 +133,24 @@ __device__ __forceinline__ uint8_t encode1(float a)
 }
 
 // ---------------------------------------------------------------------------
+// Exact FP8 decode by bit assembly (finite codes; NaN and inf codes are out
+// of contract).  E4M3: exponent field 0 is m * 2^-9, else (1 + m/8) *
+// 2^(e-7); E5M2: exponent field 0 is m * 2^-16, else (1 + m/4) * 2^(e-15).
+template <int FMT> __device__ __forceinline__ float fp8_decode(uint32_t code);
+template <> __device__ __forceinline__ float fp8_decode<FMT_E4M3>(uint32_t code)
+{
+    const uint32_t s = (code & 0x80u) << 24, e = (code >> 3) & 0xFu, m = code & 7u;
+    const float mag = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+template <> __device__ __forceinline__ float fp8_decode<FMT_E5M2>(uint32_t code)
+{
+    const uint32_t s = (code & 0x80u) << 24, e = (code >> 2) & 0x1Fu, m = code & 3u;
+    const float mag = e == 0 ? (float)m * 0x1p-16f : __uint_as_float(((e + 112u) << 23) | (m << 21));
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// ---------------------------------------------------------------------------
 // Wave64 / workgroup reductions of unsigned maxima.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {

@@ -335,6 +335,10 @@ struct Epilogue {
     {
         if (p.bias_dt == DT_FP32) return static_cast<const float *>(p.bias)[col];
         if (p.bias_dt == DT_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p.bias)[col] << 16);
+        if (p.bias_dt == BIAS_Q_E4M3)
+            return fp8_decode<FMT_E4M3>(static_cast<const uint8_t *>(p.bias)[col]) * p.bias_scale[0];
+        if (p.bias_dt == BIAS_Q_E5M2)
+            return fp8_decode<FMT_E5M2>(static_cast<const uint8_t *>(p.bias)[col]) * p.bias_scale[0];
         return 0.0f;
     }
 

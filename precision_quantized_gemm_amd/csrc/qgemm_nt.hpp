@@ -145,6 +145,15 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
                 v[8 * q + 2 * e + 1] += bf16_hi(xs[e]);
             }
         }
+    } else if (p.bias_dt == BIAS_Q_E4M3 || p.bias_dt == BIAS_Q_E5M2) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.bias) + col);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+        const float bs = p.bias_scale[0];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t c = (xs[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+            v[e] += (p.bias_dt == BIAS_Q_E4M3 ? fp8_decode<FMT_E4M3>(c) : fp8_decode<FMT_E5M2>(c)) * bs;
+        }
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) { const uint32_t b = absbits_f32(v[e]); vmax = b > vmax ? b : vmax; }

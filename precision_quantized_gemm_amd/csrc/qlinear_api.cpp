@@ -330,6 +330,43 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
     return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
 }
 
+ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
+                                  const void *w_q, int64_t N, const float *sw,
+                                  const void *bias, ql_dtype bias_dt, const float *bias_scale,
+                                  ql_qfmt fmt, const float *sx_in,
+                                  void *out, ql_dtype out_dt, const float *out_scale, float *out_amax,
+                                  void *x_q, float *sx, float *amax_x, void *ws, void *stream)
+{
+    if (!valid_fmt(fmt)) return fail(QL_ERR_VALUE, "linear_forward_static: unsupported format %d", fmt);
+    if (fmt == QL_FMT_INT8) return fail(QL_ERR_DTYPE, "linear_forward_static: FP8 formats only");
+    if (!ws) return fail(QL_ERR_NULL, "linear_forward_static: a workspace is required");
+    if (!sx || !amax_x) return fail(QL_ERR_NULL, "linear_forward_static: sx and amax_x are required outputs");
+    if (!sw) return fail(QL_ERR_NULL, "linear_forward_static: sw (the weight's step) is required");
+    ql_status st = check_quantize(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, ws);
+    if (st != QL_OK) return st;
+    const bool qbias = bias && bias_scale;
+    // A quantized bias is checked as "no bias" here and attached below.
+    GemmArgs g{x_q, fmt, QL_K_MAJOR, K, w_q, fmt, QL_K_MAJOR, K, M, N, K,
+               sx_in ? sx_in : sx, QL_PER_TENSOR, sw, QL_PER_TENSOR,
+               qbias ? nullptr : bias, bias_dt, out, out_dt, N, out_scale, out_amax, ws};
+    st = check_gemm(g);
+    if (st != QL_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ql::QzParams px = make_qz(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, amax_x,
+                              ql::ws_slot(ws, ql::WS_SLOT_QA));
+    hipError_t e = ql::launch_quantize(px, x_dt, fmt, s);
+    if (e != hipSuccess) return hip_status(e, "linear_forward_static: quantize x");
+    ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
+    if (qbias && out_dt != QL_DT_INT32) {
+        pg.bias = bias;
+        pg.bias_dt = fmt == QL_FMT_E4M3 ? ql::BIAS_Q_E4M3 : ql::BIAS_Q_E5M2;
+        pg.bias_scale = bias_scale;
+        pg.bias_vec16 = aligned16(bias);
+    }
+    return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward_static: qgemm");
+}
+
 ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
                              const void *x_q, ql_qfmt x_fmt, const float *sx,
                              const void *w_q, ql_qfmt w_fmt, const float *sw, int64_t K,

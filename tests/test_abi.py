@@ -25,8 +25,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring",
-                                  "ql_qgemm", "ql_linear_forward", "ql_linear_backward", "ql_status_string",
-                                  "ql_last_error"])
+                                  "ql_qgemm", "ql_linear_forward", "ql_linear_backward", "ql_linear_forward_static",
+                                  "ql_status_string", "ql_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -202,4 +202,27 @@ def _bwd(**kw):
 ])
 def test_linear_backward_validation(kw, status):
     assert _bwd(**kw) == status
+    assert q.ql_last_error()
+
+
+def _static(**kw):
+    a = dict(x=P, x_dt=0, M=64, K=32, w_q=Q, N=48, sw=P, bias=P, bias_dt=1, bias_scale=None, fmt=0, sx_in=None,
+             out=Q, out_dt=0, out_scale=None, out_amax=None, x_q=Q, sx=P, amax_x=P, ws=P, stream=None)
+    a.update(kw)
+    return _st("ql_linear_forward_static", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=2), _lib.QL_ERR_DTYPE),             # static inference is FP8
+    (dict(fmt=7), _lib.QL_ERR_VALUE),
+    (dict(sw=None), _lib.QL_ERR_NULL),
+    (dict(w_q=None), _lib.QL_ERR_NULL),
+    (dict(ws=None), _lib.QL_ERR_NULL),
+    (dict(sx=None), _lib.QL_ERR_NULL),
+    (dict(bias_dt=2), _lib.QL_ERR_DTYPE),         # value bias must be BF16/FP32 without bias_scale
+    (dict(out_dt=2), _lib.QL_ERR_NULL),           # E4M3 output needs out_scale
+    (dict(x_dt=3), _lib.QL_ERR_DTYPE),
+])
+def test_linear_forward_static_validation(kw, status):
+    assert _static(**kw) == status
     assert q.ql_last_error()

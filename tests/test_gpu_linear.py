@@ -150,3 +150,53 @@ def test_linear_backward_ragged_masks(orc, masks):
     w_q, sw, _ = orc.quantize(synth.bf16_bits(synth.random_bf16(81, 2, N, K, 0.05)), 0, 0)
     _backward_case(orc, g, x_q, float(sx[0]), w_q, float(sw[0]), masks, sg_in=2.0 ** -12, out_dtype="fp32",
                    what=f"ragged {masks}")
+
+
+@pytest.mark.parametrize("M,N,K,fmt,bias_kind", [
+    (512, 128, 128, 0, "q"),            # tiny layer: general kernel
+    (4096, 4096, 512, 0, "q"),          # whole tiles: pipelined kernel, fast epilogue
+    (4096, 4096, 512, 1, "q"),          # E5M2 layer and bias
+    (4133, 4112, 384, 0, "fp32"),       # ragged edge tiles, value bias
+    (4096, 4096, 256, 1, None),
+])
+def test_linear_forward_static(orc, M, N, K, fmt, bias_kind):
+    """Static FP8 inference: the weight (and the bias, with its own step)
+    arrive quantized; only x is quantized.  x's codes, step and amax bit for
+    bit; outputs at sampled entries within the float bound, with the
+    quantized bias decoded as dec(code) * bias_scale."""
+    dev = "cuda"
+    x = synth.random_bf16(91, 0, M, K)
+    w = synth.random_bf16(91, 1, N, K, 0.05)
+    w_q, sw, _ = orc.quantize(synth.bf16_bits(w), 0, fmt)
+    b32 = synth.random_fp32(91, 2, 1, N, 0.3)
+    if bias_kind == "q":
+        b_q, bs, _ = orc.quantize(b32.numpy(), 0, fmt)
+        bias_t, bscale_t = torch.from_numpy(b_q.ravel()).to(dev), torch.from_numpy(bs).to(dev)
+        ref_bias_q, ref_bs = b_q.ravel(), float(bs[0])
+    elif bias_kind == "fp32":
+        bias_t, bscale_t = b32.ravel().to(dev), None
+        ref_bias_q, ref_bs = None, None
+    else:
+        bias_t = bscale_t = ref_bias_q = ref_bs = None
+    r = q.linear_forward_static(x.to(dev), torch.from_numpy(w_q).to(dev), torch.from_numpy(sw).to(dev),
+                                bias=bias_t, bias_scale=bscale_t, fmt={0: "e4m3", 1: "e5m2"}[fmt])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K)
+    rows = np.array([0, M // 2, M - 1])
+    cols = np.array([0, N // 2, N - 1])
+    ms = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 2000)])
+    ns = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 2000)])
+    ref = orc.linear_forward_static(synth.bf16_bits(x), w_q, fmt, sw, ref_bias_q, ref_bs, fmt, ms=ms, ns=ns)
+    if bias_kind == "fp32":
+        ref_v = orc.epilogue(ref["acc"], ms, ns, ref["sx"], 0, sw, 0, b32.numpy().ravel())
+        bias_vals = b32.numpy().ravel().astype(np.float64)[ns]
+    else:
+        ref_v = ref["v"]
+        bias_vals = None if ref["bias"] is None else ref["bias"][ns]
+    assert np.array_equal(r.x_q.cpu().numpy(), ref["x_q"])
+    assert r.sx.cpu().numpy().view(np.uint32)[0] == ref["sx"].view(np.uint32)[0]
+    assert r.amax_x.cpu().numpy().view(np.uint32)[0] == ref["amax_x"].view(np.uint32)[0]
+    assert r.amax_w.item() == 0.0
+    got = r.out.cpu().to(torch.float64).numpy()[ms, ns]
+    print("static", check_float(got, ref_v, ref["S"], ref["H"], float(ref["sx"][0]) * float(sw[0]), K,
+                                bias=bias_vals, what=f"static {M}x{N}x{K} fmt={fmt} bias={bias_kind}"))
