@@ -79,6 +79,8 @@ def _load():
     lib.orc_amax_raw.restype = None
     lib.orc_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, vp, i64, vp, vp]
     lib.orc_quantize.restype = None
+    lib.orc_quantize_groups.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i64, vp, vp]
+    lib.orc_quantize_groups.restype = None
     lib.orc_ring_update.argtypes = [vp, i64, i64, i32, i32, flt]
     lib.orc_ring_update.restype = None
     lib.orc_qgemm_entries.argtypes = [vp, i32, i32, i64, vp, i32, i32, i64, i64, vp, vp, i64, vp, vp, vp, vp, i32, i32]
@@ -375,3 +377,51 @@ def linear_forward_static(x, w_q, w_fmt, sw, bias_q, bias_scale, fmt, sx_in=None
     v = epilogue(acc, ms, ns, sx_used, PER_TENSOR, np.asarray(sw, np.float32), PER_TENSOR, bias)
     return dict(x_q=xq, sx=sx, amax_x=ax, acc=acc, S=S, H=H, v=v, ms=np.asarray(ms), ns=np.asarray(ns),
                 sx_used=sx_used, bias=bias)
+
+
+def quantize_groups(x: np.ndarray, group_rows: int, fmt: int, scale_in: np.ndarray | None = None):
+    """One scale per group of ``group_rows`` consecutive rows ([SCMP] "API"
+    group_a / group_b; per_head = N rows of a (BH, N, D) tensor).  Returns
+    (codes, scale [ngroups], amax [ngroups])."""
+    x2, dt = _input_view(x)
+    rows, cols = x2.shape
+    if group_rows < 1:
+        raise ValueError("group_rows must be >= 1")
+    ng = (rows + group_rows - 1) // group_rows
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scale = np.zeros(ng, dtype=np.float32)
+    amax = np.zeros(ng, dtype=np.float32)
+    sin = None if scale_in is None else np.ascontiguousarray(scale_in, dtype=np.float32)
+    _load().orc_quantize_groups(_ptr(x2), dt, rows, cols, cols, group_rows, fmt,
+                                _ptr(sin) if sin is not None else None, _ptr(codes), cols, _ptr(scale), _ptr(amax))
+    return codes, scale, amax
+
+
+def qgemm_batched_entries(a, a_fmt, b, b_fmt, zs, ms, ns, sa, group_a, sb, group_b, bias=None):
+    """Batched product y[z] = (A[z] @ B[z]^T) with row-group scales, at the
+    listed (z, m, n) entries ([SCMP] "API": per_head batches (BH, N, D) and
+    N != M; group_a / group_b).  ``a`` is [batch, M, K] codes, ``b``
+    [batch, N, K] (both K-major per item).  Scale indices run over the
+    flattened rows of all batch items: sa[(z*M + m) // group_a] (group 0 =
+    one scale for everything), likewise sb.  Returns (acc, S, H, v) where
+    v = acc * sa * sb (+ bias[n]) in double."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    zs, ms, ns = (np.asarray(t, np.int64) for t in (zs, ms, ns))
+    batch, M, K = a.shape
+    N = b.shape[1]
+    acc = np.zeros(zs.size); S = np.zeros(zs.size); H = np.zeros(zs.size)
+    for z in np.unique(zs):
+        sel = zs == z
+        ac, s_, _, h_ = qgemm_entries(a[z], a_fmt, K_MAJOR, b[z], b_fmt, K_MAJOR, K, ms[sel], ns[sel])
+        acc[sel], S[sel], H[sel] = ac, s_, h_
+    sa = np.asarray(sa, np.float32).astype(np.float64)
+    sb = np.asarray(sb, np.float32).astype(np.float64)
+    ia = np.zeros_like(ms) if group_a == 0 else (zs * M + ms) // group_a
+    ib = np.zeros_like(ns) if group_b == 0 else (zs * N + ns) // group_b
+    v = acc * sa[ia] * sb[ib]
+    if bias is not None:
+        bv = np.asarray(bias)
+        bv = (bv.astype(np.uint32) << 16).view(np.float32) if bv.dtype == np.uint16 else bv.astype(np.float32)
+        v = v + bv.astype(np.float64)[ns]
+    return acc, S, H, v

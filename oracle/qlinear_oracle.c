@@ -235,6 +235,41 @@ void orc_quantize(const void *x, int dt, int64_t rows, int64_t cols, int64_t ldx
 }
 
 /* ------------------------------------------------------------------------ */
+/* Row-group quantization ([SCMP] "API": group_a / group_b, the row-group
+ * size of an operand's scales; per_head on a (BH, N, D) tensor is one scale
+ * per N consecutive rows of the flattened [BH*N, D]).  One scale per group
+ * of group_rows consecutive rows (the last group may be shorter); within a
+ * group, steps 1-4 exactly as for a tensor.                                */
+void orc_quantize_groups(const void *x, int dt, int64_t rows, int64_t cols, int64_t ldx,
+                         int64_t group_rows, int fmt, const float *scale_in,
+                         uint8_t *xq, int64_t ldq, float *scale_out, float *amax_out)
+{
+    int64_t ngroups = rows == 0 ? 0 : (rows + group_rows - 1) / group_rows;
+    float floor_f = orc_amax_floor(fmt);
+    double qmax = orc_qmax(fmt);
+    for (int64_t g = 0; g < ngroups; ++g) {
+        int64_t r0 = g * group_rows, r1 = r0 + group_rows < rows ? r0 + group_rows : rows;
+        double m = 0.0;
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t c = 0; c < cols; ++c) {
+                double a = fabs(orc_load(x, dt, r * ldx + c));
+                if (a > m || isnan(a)) m = a;
+            }
+        float amax = (float)m;
+        if (!(amax >= floor_f) && !isnan(amax)) amax = floor_f;
+        amax_out[g] = amax;
+        scale_out[g] = (float)((double)amax / qmax);
+        float scale = scale_in ? scale_in[g] : scale_out[g];
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t c = 0; c < cols; ++c) {
+                float v = orc_div_f32((float)orc_load(x, dt, r * ldx + c), scale);
+                int code = fmt == ORC_INT8 ? (orc_int8_encode((double)v) & 0xFF) : orc_fp8_encode((double)v, fmt);
+                xq[r * ldq + c] = (uint8_t)code;
+            }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Delayed-scaling amax history ("scale ring").  [FP8PY] linear_forward_fp8
  * and linear_backward_fp8 docstrings: the ring is a float32 buffer holding
  * an amax history and the scale; the quantize of step t casts with the

@@ -212,3 +212,17 @@ def test_qbias_values_match_decode(orc, fmt):
     ok = np.isfinite(dec)
     got = orc.qbias_values(codes[ok], fmt, 0.25)
     assert np.array_equal(got, dec[ok] * 0.25)
+
+
+def test_batched_handworked(orc):
+    """Per-head batched product with per-head steps
+    (tests/golden/groups_handworked.txt)."""
+    g = {r[0]: r[1:] for r in read_golden("groups_handworked.txt")}
+    a = np.array([int(c, 16) for c in g["batch_a"]], np.uint8).reshape(2, 1, 2)
+    b = np.array([int(c, 16) for c in g["batch_b"]], np.uint8).reshape(2, 2, 2)
+    zs, ms, ns = np.array([0, 0, 1, 1]), np.array([0, 0, 0, 0]), np.array([0, 1, 0, 1])
+    sa = [float(v) for v in g["batch_sa"]]
+    sb = [float(v) for v in g["batch_sb"]]
+    acc, S, H, v = orc.qgemm_batched_entries(a, orc.E4M3, b, orc.E4M3, zs, ms, ns, sa, 1, sb, 2)
+    assert list(acc) == [float(x) for x in g["batch_acc"]]
+    assert list(v) == [float(x) for x in g["batch_v"]]

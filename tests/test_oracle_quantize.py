@@ -221,3 +221,26 @@ def test_ring_zero_history_closed_form(orc, fmt, margin):
     assert np.all((codes == 0) | (codes == 0x80) if fmt != 2 else codes == 0)
     expect = np.float32(np.float32(np.float64(floor) / orc.qmax(fmt)) * np.float32(2.0 ** margin))
     assert ring[4] == expect
+
+
+def test_groups_handworked(orc):
+    """INT8 row groups of 2 rows (tests/golden/groups_handworked.txt)."""
+    g = {r[0]: r[1:] for r in read_golden("groups_handworked.txt")}
+    x = np.array([float(v) for v in g["group_x"]], np.float32).reshape(4, 2)
+    codes, scale, _ = orc.quantize_groups(x, 2, 2)
+    assert list(codes.view(np.int8).ravel()) == [int(v) for v in g["group_codes"]]
+    assert list(scale) == [float(v) for v in g["group_scale"]]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_groups_reduce_to_row_and_tensor(orc, fmt):
+    """Groups of one row are per-row quantization; one group of every row is
+    per-tensor; a group size that does not divide the rows leaves a short
+    last group equal to a per-tensor quantize of those rows."""
+    x = synth.bf16_bits(synth.random_bf16(5, 0, 37, 29, 3.0))
+    for G, ref in ((1, orc.quantize(x, orc.PER_ROW, fmt)), (37, orc.quantize(x, orc.PER_TENSOR, fmt))):
+        got = orc.quantize_groups(x, G, fmt)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]) and np.array_equal(got[2], ref[2])
+    got = orc.quantize_groups(x, 8, fmt)
+    tail = orc.quantize(np.ascontiguousarray(x[32:]), orc.PER_TENSOR, fmt)
+    assert np.array_equal(got[0][32:], tail[0]) and got[1][4] == tail[1][0]
