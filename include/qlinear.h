@@ -237,6 +237,59 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                             void *ws, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ql_quantize_groups -- one scale per group of rows.
+ *
+ * [SCMP] "API": group_a / group_b set the row-group size of an operand's
+ * scales, and granularity per_head quantizes a (BH, N, D) operand one head
+ * at a time.  Both are row groups of the flattened matrix: group_rows = 1
+ * is per-row, = rows per-tensor, = N per head of [BH*N, D].
+ *
+ *   x, x_dt, rows, cols, ldx, fmt, x_q, ldq: as ql_quantize.
+ *   group_rows >= 1: rows [g*G, min((g+1)*G, rows)) share scale g.
+ *   scale_in NULL (current scaling) or [ngroups] delayed steps.
+ *   scale_out, amax_out [ngroups], ngroups = ceil(rows / G): as ql_quantize
+ *            per group (scale_out may be NULL only with scale_in).
+ * One workgroup per group: meant for groups of up to a few hundred
+ * thousand elements (heads, row groups); use ql_quantize for a whole large
+ * tensor.  No workspace is needed.
+ * Errors: as ql_quantize, plus QL_ERR_VALUE for group_rows < 1.
+ * ---------------------------------------------------------------------- */
+ql_status ql_quantize_groups(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
+                             int64_t group_rows, ql_qfmt fmt, const float *scale_in,
+                             void *x_q, int64_t ldq, float *scale_out, float *amax_out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * ql_qgemm_batched -- batched scaled GEMM with row-group scales.
+ *
+ * [SCMP] "API" (per_head: (BH, N, D) operands, N != M allowed; group_a /
+ * group_b): out[z] = (A[z] . B[z]^T) * sa * sb (+ bias) for z < batch, each
+ * item exactly as ql_qgemm (layouts, formats, epilogue, outputs).
+ *
+ *   a_q + z*stride_a, b_q + z*stride_b: item z's operands (strides in
+ *            elements = bytes); out + z*stride_out (elements of out_dt).
+ *   batch    1 .. 65535.
+ *   sa, group_a: scale of A row m of item z is sa[(z*M + m) / group_a]
+ *            (row groups over the flattened batch; group_a = M gives one
+ *            scale per item, i.e. per head; 0 = one scale sa[0] for all).
+ *            sa holds ceil(batch*M / group_a) floats (1 when group_a is
+ *            0); sb, group_b likewise with z*N + n.
+ *   bias [N] shared by all items; out_amax covers every item.
+ * Operand items may overlap; output items must not.  Strides that are not
+ * multiples of 16 bytes are accepted and take the unaligned (slower)
+ * staging.  Items take the general kernel (the pipelined one serves
+ * batch == 1).
+ * Errors: as ql_qgemm, plus QL_ERR_VALUE for batch, group or stride out of
+ * range.
+ * ---------------------------------------------------------------------- */
+ql_status ql_qgemm_batched(const void *a_q, ql_qfmt a_fmt, ql_layout a_lay, int64_t lda, int64_t stride_a,
+                           const void *b_q, ql_qfmt b_fmt, ql_layout b_lay, int64_t ldb, int64_t stride_b,
+                           int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const float *sa, int64_t group_a, const float *sb, int64_t group_b,
+                           const void *bias, ql_dtype bias_dt,
+                           void *out, ql_dtype out_dt, int64_t ldo, int64_t stride_out,
+                           const float *out_scale, float *out_amax, void *ws, void *stream);
+
+/* ------------------------------------------------------------------------
  * ql_linear_forward_static -- static FP8 inference.
  *
  * [FP8PY] linear_forward_fp8 docstring: for static inference the weight

@@ -59,6 +59,11 @@ def load():
     lib.ql_linear_forward.argtypes = [vp, i32, i64, i64, vp, i64, vp, i32, i32, vp, vp,
                                       vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_forward.restype = i32
+    lib.ql_quantize_groups.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i64, vp, vp, vp]
+    lib.ql_quantize_groups.restype = i32
+    lib.ql_qgemm_batched.argtypes = [vp, i32, i32, i64, i64, vp, i32, i32, i64, i64, i64, i64, i64, i64,
+                                     vp, i64, vp, i64, vp, i32, vp, i32, i64, i64, vp, vp, vp, vp]
+    lib.ql_qgemm_batched.restype = i32
     lib.ql_linear_forward_static.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, vp, i32, vp,
                                              vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_forward_static.restype = i32
@@ -117,6 +122,20 @@ def ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out
     _check(load().ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out,
                                     out_dt, out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w,
                                     ws, stream), "ql_linear_forward")
+
+
+def ql_quantize_groups(x, x_dt, rows, cols, ldx, group_rows, fmt, scale_in, x_q, ldq, scale_out, amax_out,
+                       stream=0) -> None:
+    _check(load().ql_quantize_groups(x, x_dt, rows, cols, ldx, group_rows, fmt, scale_in, x_q, ldq, scale_out,
+                                     amax_out, stream), "ql_quantize_groups")
+
+
+def ql_qgemm_batched(a_q, a_fmt, a_lay, lda, stride_a, b_q, b_fmt, b_lay, ldb, stride_b, batch, M, N, K,
+                     sa, group_a, sb, group_b, bias, bias_dt, out, out_dt, ldo, stride_out, out_scale, out_amax,
+                     ws, stream=0) -> None:
+    _check(load().ql_qgemm_batched(a_q, a_fmt, a_lay, lda, stride_a, b_q, b_fmt, b_lay, ldb, stride_b, batch, M,
+                                   N, K, sa, group_a, sb, group_b, bias, bias_dt, out, out_dt, ldo, stride_out,
+                                   out_scale, out_amax, ws, stream), "ql_qgemm_batched")
 
 
 def ql_linear_forward_static(x, x_dt, M, K, w_q, N, sw, bias, bias_dt, bias_scale, fmt, sx_in, out, out_dt,

@@ -127,6 +127,53 @@ def quantize_ring(x: torch.Tensor, fmt, ring: torch.Tensor, idx: int, margin: in
     return x_q, scale_used, amax
 
 
+def quantize_groups(x: torch.Tensor, group_rows: int, fmt="e4m3", scale_in=None):
+    """One scale per ``group_rows`` consecutive rows of ``x`` (2-D, or 3-D
+    (BH, N, D) flattened to rows: ``group_rows = N`` quantizes per head).
+    Returns (x_q with x's shape, scale [ngroups], amax [ngroups])."""
+    if x.dtype not in _IN_DT:
+        raise TypeError(f"quantize_groups requires bf16 or fp32 input, got {x.dtype}")
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1]).contiguous()
+    rows, cols = x2.shape
+    f = _enum(FMTS, fmt, "format")
+    ng = (rows + group_rows - 1) // group_rows if group_rows > 0 else 0
+    x_q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(ng, dtype=torch.float32, device=x.device)
+    amax = torch.empty(ng, dtype=torch.float32, device=x.device)
+    _lib.ql_quantize_groups(x2.data_ptr(), _IN_DT[x.dtype], rows, cols, cols, group_rows, f, _ptr(scale_in),
+                            x_q.data_ptr(), cols, scale.data_ptr(), amax.data_ptr(), _stream())
+    return x_q.reshape(shape), scale, amax
+
+
+def qgemm_batched(a_q, a_fmt, b_q, b_fmt, sa, sb, *, group_a=0, group_b=0, bias=None, out_dtype="bf16",
+                  out_scale=None, out_amax=False, ws=None):
+    """out[z] = (A[z] @ B[z]^T) * sa * sb (+ bias) for K-major codes a_q
+    [batch, M, K] and b_q [batch, N, K]; scale of A row m of item z is
+    sa[(z*M + m) // group_a] (group_a = M: per head; 0: one scale), likewise
+    sb.  Returns out [batch, M, N] or (out, amax)."""
+    if a_q.dim() != 3 or b_q.dim() != 3 or a_q.shape[0] != b_q.shape[0] or a_q.shape[2] != b_q.shape[2]:
+        raise ValueError("qgemm_batched takes a_q [batch, M, K] and b_q [batch, N, K]")
+    a_q, b_q = a_q.contiguous(), b_q.contiguous()
+    batch, M, K = a_q.shape
+    N = b_q.shape[1]
+    odt, tdt = _OUT_DT[out_dtype]
+    out = torch.empty((batch, M, N), dtype=tdt, device=a_q.device)
+    amax = torch.empty(1, dtype=torch.float32, device=a_q.device) if out_amax else None
+    bias_dt = 0
+    if bias is not None:
+        if bias.dtype not in _IN_DT:
+            raise TypeError(f"bias must be bf16 or fp32, got {bias.dtype}")
+        bias_dt = _IN_DT[bias.dtype]
+    if ws is None and out_amax:
+        ws = workspace(a_q.device)
+    _lib.ql_qgemm_batched(a_q.data_ptr(), _enum(FMTS, a_fmt, "format"), QL_K_MAJOR, K, M * K,
+                          b_q.data_ptr(), _enum(FMTS, b_fmt, "format"), QL_K_MAJOR, K, N * K, batch, M, N, K,
+                          _ptr(sa), group_a, _ptr(sb), group_b, _ptr(bias), bias_dt, out.data_ptr(), odt, N, M * N,
+                          _ptr(out_scale), _ptr(amax), _ptr(ws), _stream())
+    return (out, amax) if out_amax else out
+
+
 def qgemm(a_q, a_fmt, b_q, b_fmt, sa, sb, *, a_layout="k_major", b_layout="k_major",
           sa_granularity="per_tensor", sb_granularity="per_tensor", bias=None,
           out_dtype="bf16", out_scale=None, out_amax=False, K=None, ws=None):

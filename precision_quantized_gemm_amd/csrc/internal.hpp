@@ -37,7 +37,8 @@ struct QzParams {
     int64_t n_units;          // 16-element vector units (flat / rows modes)
     int64_t units_per_row;    // cols / 16 (rows mode, per-row vector path)
     int mode;                 // 0 flat-vector, 1 rows-vector, 2 scalar
-    int per_row;
+    int per_row;              // one scale per group of group_rows rows (per row: 1)
+    int64_t group_rows;
     int vec_rows;             // per-row kernel may use 16-byte units
     int delayed;
     // Delayed scaling with an amax history ring [hist (hist_len) | scale]:
@@ -60,7 +61,13 @@ struct GemmParams {
     int64_t lda, ldb;
     int64_t M, N, K;
     const float *sa, *sb;
-    int64_t sa_stride, sb_stride;   // 0 (per tensor) or 1 (per row)
+    int64_t sa_group, sb_group;     // rows per scale: 0 (one scale), 1 (per row), G (row groups)
+    // Batched products (grid y = batch index z): item z reads a + z*stride_a,
+    // b + z*stride_b and writes out + z*stride_out (elements); its scale
+    // rows are z*M + m and z*N + n of the flattened batch.
+    int64_t batch;                  // batch items (grid y); 1 for a single product
+    int64_t stride_a, stride_b, stride_out;
+    int64_t row_base, col_base;     // z*M, z*N (set in the kernel)
     const void *bias;
     int bias_dt;                    // -1 none, 0 BF16, 1 FP32, BIAS_Q_E4M3 / BIAS_Q_E5M2 codes
     const float *bias_scale;        // step of a quantized bias ([1])

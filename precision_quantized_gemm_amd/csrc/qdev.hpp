@@ -182,7 +182,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 //
 // Every workgroup folds its maximum into slot[0] with a device-scope atomic
 // max, then increments slot[1] with an acquire-release device-scope atomic.
-// The workgroup that sees the count reach gridDim.x - 1 is the last one: the
+// The workgroup that sees the count reach the grid size - 1 is the last one: the
 // release/acquire pair orders every other workgroup's max before its read,
 // across all XCDs (their L2s are not coherent without device-scope
 // ordering).  It returns the final maximum and leaves the slot zeroed for the
@@ -198,7 +198,7 @@ __device__ __forceinline__ bool elect_last_max(uint32_t *slot, uint32_t block_ma
 {
     __hip_atomic_fetch_max(&slot[0], block_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t prev = __hip_atomic_fetch_add(&slot[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev != gridDim.x - 1) return false;
+    if (prev != gridDim.x * gridDim.y - 1) return false;
     *result = __hip_atomic_load(&slot[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&slot[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&slot[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

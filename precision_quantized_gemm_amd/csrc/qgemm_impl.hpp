@@ -327,7 +327,7 @@ struct Epilogue {
     __device__ __forceinline__ explicit Epilogue(const GemmParams &pp) : p(pp)
     {
         inv_os = pp.out_dt == DT_E4M3 ? 1.0f / pp.out_scale[0] : 1.0f;
-        per_tensor = pp.sa_stride == 0 && pp.sb_stride == 0;
+        per_tensor = pp.sa_group == 0 && pp.sb_group == 0;
         s_ab = (per_tensor && pp.out_dt != DT_INT32) ? pp.sa[0] * pp.sb[0] : 1.0f;
     }
 
@@ -359,12 +359,12 @@ struct Epilogue {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e])) * s_ab;
         } else {
-            const float s_row = p.sa[row * p.sa_stride];
+            const float s_row = p.sa[p.sa_group ? (p.row_base + row) / p.sa_group : 0];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t c = col + (e < n ? e : 0);
                 const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
-                v[e] = a * s_row * p.sb[c * p.sb_stride];
+                v[e] = a * s_row * p.sb[p.sb_group ? (p.col_base + c) / p.sb_group : 0];
             }
         }
         if (p.bias_dt >= 0) {
@@ -425,6 +425,16 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
     __shared__ uint32_t red[GEMM_THREADS / 64];
 
+    // Batch item z (grid y): its operands, its output and its scale rows.
+    {
+        const int64_t z = blockIdx.y;
+        const int eb = p.out_dt == DT_BF16 ? 2 : p.out_dt == DT_E4M3 ? 1 : 4;
+        p.a += z * p.stride_a;
+        p.b += z * p.stride_b;
+        p.out = static_cast<char *>(p.out) + z * p.stride_out * eb;
+        p.row_base = z * p.M;
+        p.col_base = z * p.N;
+    }
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -527,7 +537,8 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
         p.tiles_m = p.tiles_n = 1;
     }
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST>), dim3((unsigned)grid),
+    const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
+    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
     return hipGetLastError();
 }
@@ -545,7 +556,7 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
     // The pipelined kernel covers FP8 only: INT8's paired 32-deep MFMAs do
     // not fit its register budget.
     if constexpr (AF != FMT_INT8)
-        if (p.fast && !A_MN && !B_MN && big >= 256) return launch_nt<AF, BF>(p, s);
+        if (p.fast && !A_MN && !B_MN && big >= 256 && p.batch <= 1) return launch_nt<AF, BF>(p, s);
     if (p.fast) {
         if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
         return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);

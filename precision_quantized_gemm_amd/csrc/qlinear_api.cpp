@@ -113,6 +113,7 @@ ql::QzParams make_qz(const void *x, int x_dt, int64_t rows, int64_t cols, int64_
     p.floor = fmt_floor(fmt);
     p.n_elems = rows * cols;
     p.per_row = gran == QL_PER_ROW;
+    p.group_rows = 1;
     p.delayed = scale_in != nullptr;
     const bool al = aligned16(x) && aligned16(x_q);
     const bool flat = (ldx == cols && ldq == cols) || rows <= 1;
@@ -194,8 +195,9 @@ ql::GemmParams make_gemm(const GemmArgs &g, uint32_t *slot)
     p.lda = g.lda; p.ldb = g.ldb;
     p.M = g.M; p.N = g.N; p.K = g.K;
     p.sa = g.sa; p.sb = g.sb;
-    p.sa_stride = g.sa_gran == QL_PER_ROW ? 1 : 0;
-    p.sb_stride = g.sb_gran == QL_PER_ROW ? 1 : 0;
+    p.sa_group = g.sa_gran == QL_PER_ROW ? 1 : 0;
+    p.sb_group = g.sb_gran == QL_PER_ROW ? 1 : 0;
+    p.batch = 1;
     p.bias = g.out_dt == QL_DT_INT32 ? nullptr : g.bias;
     p.bias_dt = p.bias ? g.bias_dt : -1;
     p.out = g.out; p.ldo = g.ldo; p.out_dt = g.out_dt;
@@ -328,6 +330,60 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
     if (e != hipSuccess) return hip_status(e, "linear_forward: quantize w");
     ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
     return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
+}
+
+ql_status ql_quantize_groups(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
+                             int64_t group_rows, ql_qfmt fmt, const float *scale_in,
+                             void *x_q, int64_t ldq, float *scale_out, float *amax_out, void *stream)
+{
+    if (group_rows < 1) return fail(QL_ERR_VALUE, "quantize_groups: group_rows %lld must be >= 1", (long long)group_rows);
+    // Validated as a per-row quantize (no workspace: groups need no election).
+    ql_status st = check_quantize(x, x_dt, rows, cols, ldx, QL_PER_ROW, fmt, scale_in, x_q, ldq, scale_out, nullptr);
+    if (st != QL_OK) return st;
+    if ((rows + group_rows - 1) / group_rows > 0x7FFFFFFF)
+        return fail(QL_ERR_UNSUPPORTED, "quantize_groups: at most 2^31-1 groups");
+    ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, QL_PER_ROW, fmt, scale_in, x_q, ldq, scale_out, amax_out,
+                             nullptr);
+    p.group_rows = group_rows;
+    return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize_groups launch");
+}
+
+ql_status ql_qgemm_batched(const void *a_q, ql_qfmt a_fmt, ql_layout a_lay, int64_t lda, int64_t stride_a,
+                           const void *b_q, ql_qfmt b_fmt, ql_layout b_lay, int64_t ldb, int64_t stride_b,
+                           int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const float *sa, int64_t group_a, const float *sb, int64_t group_b,
+                           const void *bias, ql_dtype bias_dt,
+                           void *out, ql_dtype out_dt, int64_t ldo, int64_t stride_out,
+                           const float *out_scale, float *out_amax, void *ws, void *stream)
+{
+    if (batch < 1 || batch > 65535)
+        return fail(QL_ERR_VALUE, "qgemm_batched: batch %lld outside [1, 65535]", (long long)batch);
+    if (group_a < 0 || group_b < 0)
+        return fail(QL_ERR_VALUE, "qgemm_batched: negative scale group size");
+    if (stride_a < 0 || stride_b < 0 || stride_out < 0)
+        return fail(QL_ERR_VALUE, "qgemm_batched: negative batch stride");
+    // Each item is checked as one product; the scale granularity is checked
+    // through the group sizes above.
+    GemmArgs g{a_q, a_fmt, a_lay, lda, b_q, b_fmt, b_lay, ldb, M, N, K, sa, QL_PER_TENSOR, sb, QL_PER_TENSOR,
+               bias, bias_dt, out, out_dt, ldo, out_scale, out_amax, ws};
+    ql_status st = check_gemm(g);
+    if (st != QL_OK) return st;
+    uint32_t *slot = ws ? ql::ws_slot(ws, ql::WS_SLOT_GEMM) : nullptr;
+    ql::GemmParams p = make_gemm(g, slot);
+    p.sa_group = group_a;
+    p.sb_group = group_b;
+    p.batch = batch;
+    p.stride_a = stride_a;
+    p.stride_b = stride_b;
+    p.stride_out = stride_out;
+    // Every item's base must keep the alignment the vector paths assume.
+    if (stride_a % 16) { p.a_aligned = false; p.fast = false; }
+    if (stride_b % 16) { p.b_aligned = false; p.fast = false; }
+    const int eb = out_elem_bytes(out_dt);
+    if (stride_out % 4) p.out_vec4 = false;
+    if ((stride_out * eb) % 16) p.out_vec16 = false;
+    return hip_status(ql::launch_qgemm(p, a_fmt, b_fmt, a_lay == QL_MN_MAJOR, b_lay == QL_MN_MAJOR,
+                                       static_cast<hipStream_t>(stream)), "qgemm_batched launch");
 }
 
 ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int64_t K,

@@ -18,7 +18,8 @@
 //             pass 2 it walks the tensor from the end backwards, so it
 //             starts on the data pass 1 read last, which the memory-side
 //             cache (256 MB) still holds.
-//   qz_rows   per-row: one workgroup per row; the row's second read hits
+//   qz_rows   per-row and row groups: one workgroup per group of rows
+//             (one row for per-row scales); the group's second read hits
 //             the cache, so HBM sees each element once.
 #include "qdev.hpp"
 #include "internal.hpp"
@@ -31,7 +32,7 @@ namespace ql {
 // keeps the end-of-grid election to 256 atomic pairs.
 constexpr int QZ_THREADS = 1024;
 constexpr int QZ_MAX_BLOCKS = 256;
-// Per-row kernel: one workgroup of 4 waves per row.
+// Per-row / row-group kernel: one workgroup of 4 waves per group of rows.
 constexpr int QZ_ROW_THREADS = 256;
 constexpr int QZ_UNIT = 16;            // elements per vector unit
 constexpr int QZ_UNROLL = 4;
@@ -273,26 +274,41 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Per-row: one workgroup per row.  Pass 1 reduces the row's amax, pass 2
-// re-reads the row (from cache) and casts it with the row's step (or the
-// caller's step under delayed scaling).
+// Per-row and row groups: one workgroup per group.  Pass 1 reduces the
+// group's amax, pass 2 re-reads the group (from cache) and casts it with the
+// group's step (or the caller's step under delayed scaling).
 template <typename T, int FMT, bool VEC, bool DELAYED>
 __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
 {
-    const int64_t row = blockIdx.x;
-    const T *x = static_cast<const T *>(p.x) + row * p.ldx;
-    uint8_t *xq = static_cast<uint8_t *>(p.xq) + row * p.ldq;
+    // Group g = blockIdx.x: rows [g*G, min((g+1)*G, rows)), G = group_rows
+    // (1 for per-row scales).
+    const int64_t grp = blockIdx.x;
+    const int64_t r0 = grp * p.group_rows;
+    const int64_t r1 = r0 + p.group_rows < p.rows ? r0 + p.group_rows : p.rows;
+    // Narrow rows (fewer work items than threads) are covered several per
+    // pass: thread t takes item t % W of row t / W, W items per row.
+    const int64_t W = VEC ? p.units_per_row : p.cols;
+    int64_t rpp = 1, tr = 0, tu = threadIdx.x, ustep = QZ_ROW_THREADS;
+    if (W > 0 && W < QZ_ROW_THREADS) {
+        const int w = (int)W;
+        rpp = QZ_ROW_THREADS / w;
+        tr = (int)threadIdx.x / w;
+        tu = (int)threadIdx.x - (int)tr * w;
+        ustep = w;
+        if (tr >= rpp) tr = r1 - r0;                // idle threads
+    }
     uint32_t m = 0;
-    if (VEC) {
-        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_ROW_THREADS) {
-            Vec16<T> v;
-            v.load(x + u * QZ_UNIT);
-            uint32_t t = v.amax_bits();
-            m = t > m ? t : m;
-        }
-    } else {
-        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_ROW_THREADS) {
-            uint32_t t = absbits_f32(load1<T>(x, c));
+    for (int64_t r = r0 + tr; r < r1; r += rpp) {
+        const T *x = static_cast<const T *>(p.x) + r * p.ldx;
+        for (int64_t u = tu; u < W; u += ustep) {
+            uint32_t t;
+            if (VEC) {
+                Vec16<T> v;
+                v.load(x + u * QZ_UNIT);
+                t = v.amax_bits();
+            } else {
+                t = absbits_f32(load1<T>(x, u));
+            }
             m = t > m ? t : m;
         }
     }
@@ -302,19 +318,22 @@ __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
     const float amax = a < p.floor ? p.floor : a;
     const float step = amax / p.qmax;                      // IEEE division
     if (threadIdx.x == 0) {
-        if (p.amax_out) p.amax_out[row] = amax;
-        if (p.scale_out) p.scale_out[row] = step;
+        if (p.amax_out) p.amax_out[grp] = amax;
+        if (p.scale_out) p.scale_out[grp] = step;
     }
-    const Divider div(DELAYED ? p.scale_src[row] : step);
-    if (VEC) {
-        for (int64_t u = threadIdx.x; u < p.units_per_row; u += QZ_ROW_THREADS) {
-            Vec16<T> v;
-            v.load(x + u * QZ_UNIT);
-            *reinterpret_cast<uint4 *>(xq + u * QZ_UNIT) = encode16<FMT>(v, div);
+    const Divider div(DELAYED ? p.scale_src[grp] : step);
+    for (int64_t r = r0 + tr; r < r1; r += rpp) {
+        const T *x = static_cast<const T *>(p.x) + r * p.ldx;
+        uint8_t *xq = static_cast<uint8_t *>(p.xq) + r * p.ldq;
+        for (int64_t u = tu; u < W; u += ustep) {
+            if (VEC) {
+                Vec16<T> v;
+                v.load(x + u * QZ_UNIT);
+                *reinterpret_cast<uint4 *>(xq + u * QZ_UNIT) = encode16<FMT>(v, div);
+            } else {
+                xq[u] = encode1<FMT>(div(load1<T>(x, u)));
+            }
         }
-    } else {
-        for (int64_t c = threadIdx.x; c < p.cols; c += QZ_ROW_THREADS)
-            xq[c] = encode1<FMT>(div(load1<T>(x, c)));
     }
 }
 
@@ -355,7 +374,7 @@ static hipError_t launch_fmt(const QzParams &p, hipStream_t s)
 {
     if (p.per_row) {
         if (p.rows == 0) return hipSuccess;
-        const dim3 grid((unsigned)p.rows);
+        const dim3 grid((unsigned)((p.rows + p.group_rows - 1) / p.group_rows));
         if (p.vec_rows) {
             if (p.delayed) hipLaunchKernelGGL((qz_rows<T, FMT, true, true>), grid, dim3(QZ_ROW_THREADS), 0, s, p);
             else hipLaunchKernelGGL((qz_rows<T, FMT, true, false>), grid, dim3(QZ_ROW_THREADS), 0, s, p);

@@ -23,6 +23,11 @@ Workloads (N(0, v) names the *variance* v):
 * ``mlp_backward``  G BF16 [2048,4096] N(0,1e-3) with ``mlp_up``'s x and W.
 * ``large_fp8``     a BF16 [16384,8192] Student-t(3); b BF16 [8192,8192]
   N(0,1/8192).
+* ``per_head``      q, k FP32 [16,196,64] N(0,1) (BH=16, N=196, D=64);
+  for the softmax.V product (N != M): p FP32 [16,196,160] U(0, 2/160)
+  (non-negative, mean 1/160 like attention weights over 160 keys) and
+  v FP32 [16,160,64] N(0,1) with head h scaled by 2^(h mod 4 - 1), so the
+  heads' ranges differ.
 
 Seeds are 0x5EED0000 + workload number (1..5); each tensor has its own
 stream id.
@@ -41,7 +46,8 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 _CHUNK = 1 << 22
 
-WORKLOAD_IDS = {"tiny_linear": 1, "rowwise_int8": 2, "mlp_up": 3, "mlp_backward": 4, "large_fp8": 5}
+WORKLOAD_IDS = {"tiny_linear": 1, "rowwise_int8": 2, "mlp_up": 3, "mlp_backward": 4, "large_fp8": 5,
+                "per_head": 6}
 
 
 def _threads() -> int:
@@ -165,6 +171,16 @@ def workload(name: str) -> dict:
         return dict(
             a=to_bf16(student_t3(s, 0, 16384 * 8192).reshape(16384, 8192)),
             b=to_bf16(normal(s, 1, 8192 * 8192, math.sqrt(1.0 / 8192)).reshape(8192, 8192)),
+        )
+    if name == "per_head":
+        bh, n, nk, d = 16, 196, 160, 64
+        v = normal(s, 3, bh * nk * d).reshape(bh, nk, d)
+        v *= (np.float32(2.0) ** (np.arange(bh) % 4 - 1).astype(np.float32))[:, None, None]
+        return dict(
+            q=torch.from_numpy(normal(s, 0, bh * n * d).reshape(bh, n, d)),
+            k=torch.from_numpy(normal(s, 1, bh * n * d).reshape(bh, n, d)),
+            p=torch.from_numpy((uniform(s, 2, 0, bh * n * nk) * (2.0 / nk)).astype(np.float32).reshape(bh, n, nk)),
+            v=torch.from_numpy(v),
         )
     raise KeyError(name)
 

@@ -26,7 +26,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring",
                                   "ql_qgemm", "ql_linear_forward", "ql_linear_backward", "ql_linear_forward_static",
-                                  "ql_status_string", "ql_last_error"])
+                                  "ql_quantize_groups", "ql_qgemm_batched", "ql_status_string", "ql_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -225,4 +225,49 @@ def _static(**kw):
 ])
 def test_linear_forward_static_validation(kw, status):
     assert _static(**kw) == status
+    assert q.ql_last_error()
+
+
+def _groups(**kw):
+    a = dict(x=P, x_dt=0, rows=40, cols=32, ldx=32, group_rows=8, fmt=0, scale_in=None, x_q=Q, ldq=32, scale_out=P,
+             amax_out=P, stream=None)
+    a.update(kw)
+    return _st("ql_quantize_groups", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group_rows=0), _lib.QL_ERR_VALUE),
+    (dict(group_rows=-3), _lib.QL_ERR_VALUE),
+    (dict(fmt=9), _lib.QL_ERR_VALUE),
+    (dict(x_dt=2), _lib.QL_ERR_DTYPE),
+    (dict(ldx=16), _lib.QL_ERR_SHAPE),
+    (dict(x_q=None), _lib.QL_ERR_NULL),
+    (dict(scale_out=None), _lib.QL_ERR_NULL),
+])
+def test_quantize_groups_validation(kw, status):
+    assert _groups(**kw) == status
+    assert q.ql_last_error()
+
+
+def _batched(**kw):
+    a = dict(a_q=P, a_fmt=0, a_lay=0, lda=64, stride_a=64 * 16, b_q=Q, b_fmt=0, b_lay=0, ldb=64, stride_b=64 * 24,
+             batch=4, M=16, N=24, K=64, sa=P, group_a=16, sb=P, group_b=24, bias=None, bias_dt=0, out=Q, out_dt=0,
+             ldo=24, stride_out=16 * 24, out_scale=None, out_amax=None, ws=None, stream=None)
+    a.update(kw)
+    return _st("ql_qgemm_batched", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), _lib.QL_ERR_VALUE),
+    (dict(batch=65536), _lib.QL_ERR_VALUE),
+    (dict(group_a=-1), _lib.QL_ERR_VALUE),
+    (dict(stride_b=-5), _lib.QL_ERR_VALUE),
+    (dict(a_fmt=2), _lib.QL_ERR_DTYPE),
+    (dict(lda=8), _lib.QL_ERR_SHAPE),
+    (dict(sa=None), _lib.QL_ERR_NULL),
+    (dict(out_dt=2), _lib.QL_ERR_NULL),
+    (dict(out_amax=P), _lib.QL_ERR_NULL),      # out_amax needs the workspace
+])
+def test_qgemm_batched_validation(kw, status):
+    assert _batched(**kw) == status
     assert q.ql_last_error()
