@@ -141,6 +141,52 @@ def time_backward(torch, q, synth, dev, reps):
             "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
 
 
+def time_per_head(torch, q, _lib, synth, dev, reps):
+    """The per-head attention products of the per-head workload (BH = 16,
+    N = 196, D = 64): per-head E4M3 quantize of q, k, p, v
+    (ql_quantize_groups), S = Q.K^T and O = P.V with N != M (V MN-major) as
+    ql_qgemm_batched with one scale per head on both operands."""
+    d = {k: v.to(dev) for k, v in synth.workload("per_head").items()}
+    BH, N, D = d["q"].shape
+    NK = d["v"].shape[1]
+    f = {}
+
+    def quant_all():
+        for role, g in (("q", N), ("k", N), ("p", N), ("v", NK)):
+            f[role] = q.quantize_groups(d[role], g, "e4m3")
+
+    quant_all()
+    s_out = torch.empty((BH, N, N), dtype=torch.bfloat16, device=dev)
+    o_out = torch.empty((BH, N, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def qk():
+        (aq, sa, _), (bq, sb, _) = f["q"], f["k"]
+        q.ql_qgemm_batched(aq.data_ptr(), _lib.QL_FMT_E4M3, _lib.QL_K_MAJOR, D, N * D,
+                           bq.data_ptr(), _lib.QL_FMT_E4M3, _lib.QL_K_MAJOR, D, N * D, BH, N, N, D,
+                           sa.data_ptr(), N, sb.data_ptr(), N, None, 0, s_out.data_ptr(), _lib.QL_DT_BF16, N, N * N,
+                           None, None, None, stream)
+
+    def pv():
+        (aq, sa, _), (vq, sv, _) = f["p"], f["v"]
+        q.ql_qgemm_batched(aq.data_ptr(), _lib.QL_FMT_E4M3, _lib.QL_K_MAJOR, NK, N * NK,
+                           vq.data_ptr(), _lib.QL_FMT_E4M3, _lib.QL_MN_MAJOR, D, NK * D, BH, N, D, NK,
+                           sa.data_ptr(), N, sv.data_ptr(), D, None, 0, o_out.data_ptr(), _lib.QL_DT_BF16, D, N * D,
+                           None, None, None, stream)
+
+    for _ in range(3):
+        quant_all(); qk(); pv()
+    ms_q = time_events(quant_all, reps, torch)
+    ms_qk = time_events(qk, reps, torch)
+    ms_pv = time_events(pv, reps, torch)
+    fl_qk, fl_pv = 2.0 * BH * N * N * D, 2.0 * BH * N * D * NK
+    return {"workload": f"per-head q,k [{BH},{N},{D}], p [{BH},{N},{NK}], v [{BH},{NK},{D}] FP32 -> E4M3 "
+                        "per head; S = Q.K^T, O = P.V (BF16 out)",
+            "quantize_4_tensors_ms": round(ms_q, 5), "qk_ms": round(ms_qk, 5), "pv_ms": round(ms_pv, 5),
+            "qk_TFLOPs": round(fl_qk / (ms_qk * 1e-3) / 1e12, 2), "pv_TFLOPs": round(fl_pv / (ms_pv * 1e-3) / 1e12, 2),
+            "note": "launch-bound sizes (tens of MFLOP per product)"}
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -312,6 +358,9 @@ def main():
         log("backward")
         bwd = time_backward(torch, q, synth, dev, args.steps)
 
+    log("per-head batched products")
+    per_head = time_per_head(torch, q, _lib, synth, dev, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -364,6 +413,7 @@ def main():
                              "TFLOPs": round(flops / (ms_static * 1e-3) / 1e12, 2),
                              "workload": "ql_linear_forward_static: quantize a, GEMM with the pre-quantized b"},
         "linear_backward": bwd,
+        "per_head": per_head,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
         "wall_s_timed_region": round(t_wall, 4),

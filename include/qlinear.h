@@ -82,12 +82,13 @@ typedef enum { QL_K_MAJOR = 0, QL_MN_MAJOR = 1 } ql_layout;
  * a counter that elects the last workgroup).  Every call that uses them
  * leaves them reset to zero, so a workspace is zeroed once, at allocation,
  * and never again (the zero-fill dispatch per quantize that [FP8PY]'s commit
- * message removes is not needed at all).  Calls that share a workspace must
- * be ordered (same stream or explicit events); concurrent calls need
- * separate workspaces.
+ * message removes is not needed at all).  Behind those words the workspace
+ * holds 1 MiB of scratch for grad_bias's partial column sums, which every
+ * use overwrites.  Calls that share a workspace must be ordered (same stream
+ * or explicit events); concurrent calls need separate workspaces.
  * ---------------------------------------------------------------------- */
 
-/* Size in bytes of one workspace (a small constant). */
+/* Size in bytes of one workspace (a constant, 1 KiB + 1 MiB). */
 size_t ql_workspace_bytes(void);
 
 /* Zero a freshly allocated workspace of `bytes` bytes on `stream` (a fill
@@ -328,7 +329,8 @@ ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int6
  * copies:
  *   dX [M, K] = (g_q . W) * sg * sw   (W read MN-major from w_q [N, K])
  *   dW [N, K] = (g_q^T . X) * sg * sx (g_q and x_q [M, K] read MN-major)
- *   dbias [N] = column sums of the BF16 g (FP32, fixed summation order)
+ *   dbias [N] = column sums of the BF16 g (FP32; the summation order
+ *            depends on M and N only, so results repeat bit for bit)
  *
  *   g        BF16 [M, N] row-major (leading dimension N).
  *   x_q, sx  forward codes of x [M, K] (leading dimension K) and their
@@ -342,7 +344,7 @@ ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int6
  *   dbias    FP32 [N], required with QL_BWD_DBIAS.
  *   g_q, sg, amax_g  g's codes [M, N] and its per-tensor step and amax, as
  *            ql_quantize writes them; required when dX or dW is produced.
- *   ws       workspace (required when dX or dW is produced).
+ *   ws       workspace (required).
  * Errors: as ql_quantize and ql_qgemm, plus QL_ERR_VALUE for a bad mask.
  * ---------------------------------------------------------------------- */
 #define QL_BWD_DX 1u

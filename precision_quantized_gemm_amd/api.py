@@ -335,7 +335,7 @@ def linear_backward(g, x_q, sx, w_q, sw, *, x_fmt="e4m3", w_fmt="e4m3", g_fmt="e
     g_q = torch.empty((M, N), dtype=torch.uint8, device=dev) if gemms else None
     sg = torch.empty(1, dtype=torch.float32, device=dev) if gemms else None
     amax_g = torch.empty(1, dtype=torch.float32, device=dev) if gemms else None
-    if ws is None and gemms:
+    if ws is None:
         ws = workspace(dev)
     g = g.contiguous()
     _lib.ql_linear_backward(g.data_ptr(), M, N, x_q.data_ptr(), _enum(FMTS, x_fmt, "format"), sx.data_ptr(),

@@ -2,43 +2,129 @@
 // column sums of the BF16 output gradient g [M, N] (AstrAI ops/fp8.py
 // linear_backward_fp8 returns grad_bias beside dX and dW).
 //
-// One workgroup owns 64 columns; its 16 waves each sum every 16th row of
-// those columns (a wave reads 128 contiguous bytes per row), and the 16
-// partial sums of a column are added in a fixed order, so the result does
-// not depend on scheduling.  FP32 accumulation: M/16 + 16 additions per
-// column.
+// Two deterministic stages, with a summation order fixed by (M, N) alone:
+//   col_sum_part  grid (column blocks of 512, S row splits).  Each lane owns
+//                 8 consecutive columns (one 16-byte load of a row); the 4
+//                 waves of a workgroup take every 4th row of the split, and
+//                 their sums are added in wave order.  With S = 1 the result
+//                 goes straight to grad_bias; else to partial row s.
+//   col_sum_final adds the S partial rows of each column in split order.
+// FP32 accumulation; a column's sum passes through at most
+// ceil(ceil(M/S)/4) + 3 + S additions.
 #include "qdev.hpp"
 #include "internal.hpp"
 
 namespace ql {
 
-constexpr int CS_COLS = 64, CS_GROUPS = 16;
+constexpr int CS_THREADS = 256;                 // 4 waves
+constexpr int CS_VEC = 8;                       // columns per lane
+constexpr int CS_COLS = 64 * CS_VEC;            // columns per workgroup
+constexpr int CS_UNROLL = 4;                    // rows in flight per lane
+constexpr int CS_MAX_SPLITS = 32;
 
-__global__ __launch_bounds__(CS_COLS * CS_GROUPS) void col_sum_bf16(const uint16_t *g, int64_t M, int64_t N,
-                                                                   int64_t ldg, float *out)
+template <bool VEC>
+__global__ __launch_bounds__(CS_THREADS) void col_sum_part(const uint16_t *g, int64_t M, int64_t N, int64_t ldg,
+                                                           int64_t rows_per_split, float *dst)
 {
-    const int cx = threadIdx.x % CS_COLS, ry = threadIdx.x / CS_COLS;
-    const int64_t col = (int64_t)blockIdx.x * CS_COLS + cx;
-    float s = 0.0f;
-    if (col < N)
-        for (int64_t r = ry; r < M; r += CS_GROUPS) s += __uint_as_float((uint32_t)g[r * ldg + col] << 16);
-    __shared__ float part[CS_GROUPS][CS_COLS + 1];
-    part[ry][cx] = s;
-    __syncthreads();
-    if (ry == 0 && col < N) {
-        float t = 0.0f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col0 = (int64_t)blockIdx.x * CS_COLS + lane * CS_VEC;
+    const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
+    const int64_t r_end = r_begin + rows_per_split < M ? r_begin + rows_per_split : M;
+    float acc[CS_VEC];
 #pragma unroll
-        for (int i = 0; i < CS_GROUPS; ++i) t += part[i][cx];
-        out[col] = t;
+    for (int e = 0; e < CS_VEC; ++e) acc[e] = 0.0f;
+
+    auto load_row = [&](int64_t r, uint32_t (&w)[4]) {
+        const uint16_t *src = g + r * ldg + col0;
+        if (VEC) {
+            if (col0 < N) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            } else {
+                w[0] = w[1] = w[2] = w[3] = 0u;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = col0 + 2 * e < N ? src[2 * e] : 0u;
+                const uint32_t hi = col0 + 2 * e + 1 < N ? src[2 * e + 1] : 0u;
+                w[e] = lo | (hi << 16);
+            }
+        }
+    };
+    auto add_row = [&](const uint32_t (&w)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_lo(w[e]);
+            acc[2 * e + 1] += bf16_hi(w[e]);
+        }
+    };
+
+    // Rows r_begin + wave + 4i, four loads in flight, added in row order.
+    int64_t r = r_begin + wave;
+    for (; r + 4 * (CS_UNROLL - 1) < r_end; r += 4 * CS_UNROLL) {
+        uint32_t w[CS_UNROLL][4];
+#pragma unroll
+        for (int u = 0; u < CS_UNROLL; ++u) load_row(r + 4 * u, w[u]);
+#pragma unroll
+        for (int u = 0; u < CS_UNROLL; ++u) add_row(w[u]);
+    }
+    for (; r < r_end; r += 4) {
+        uint32_t w[4];
+        load_row(r, w);
+        add_row(w);
+    }
+
+    __shared__ float part[4][CS_VEC][64 + 1];
+#pragma unroll
+    for (int e = 0; e < CS_VEC; ++e) part[wave][e][lane] = acc[e];
+    __syncthreads();
+    if (wave == 0) {
+        float* out = dst + (int64_t)blockIdx.y * N;
+#pragma unroll
+        for (int e = 0; e < CS_VEC; ++e) {
+            const float t = ((part[0][e][lane] + part[1][e][lane]) + part[2][e][lane]) + part[3][e][lane];
+            if (col0 + e < N) out[col0 + e] = t;
+        }
     }
 }
 
-hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, hipStream_t s)
+__global__ __launch_bounds__(256) void col_sum_final(const float *part, int64_t N, int splits, float *out)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    float t = part[col];
+    for (int s = 1; s < splits; ++s) t += part[(int64_t)s * N + col];
+    out[col] = t;
+}
+
+int col_sum_splits(int64_t M, int64_t N)
+{
+    const int64_t blocks = (N + CS_COLS - 1) / CS_COLS;
+    int64_t s = (512 + blocks - 1) / blocks;                  // about 512 workgroups
+    const int64_t by_rows = (M + 4 * CS_UNROLL - 1) / (4 * CS_UNROLL);
+    const int64_t by_ws = WS_PART_BYTES / (4 * (N > 0 ? N : 1));
+    if (s > CS_MAX_SPLITS) s = CS_MAX_SPLITS;
+    if (s > by_rows) s = by_rows;
+    if (s > by_ws) s = by_ws;
+    return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, float *partials,
+                               hipStream_t s)
 {
     if (N == 0) return hipSuccess;
-    const int64_t blocks = (N + CS_COLS - 1) / CS_COLS;
-    hipLaunchKernelGGL(col_sum_bf16, dim3((unsigned)blocks), dim3(CS_COLS * CS_GROUPS), 0, s,
-                       static_cast<const uint16_t *>(g), M, N, ldg, out);
+    const int splits = col_sum_splits(M, N);
+    const int64_t rows_per_split = splits > 1 ? (M + splits - 1) / splits : (M > 0 ? M : 1);
+    const dim3 grid((unsigned)((N + CS_COLS - 1) / CS_COLS), (unsigned)splits);
+    float *dst = splits > 1 ? partials : out;
+    const uint16_t *gp = static_cast<const uint16_t *>(g);
+    const bool vec = (reinterpret_cast<uintptr_t>(g) & 15u) == 0 && N % CS_VEC == 0 && ldg % CS_VEC == 0;
+    if (vec) hipLaunchKernelGGL(col_sum_part<true>, grid, dim3(CS_THREADS), 0, s, gp, M, N, ldg, rows_per_split, dst);
+    else hipLaunchKernelGGL(col_sum_part<false>, grid, dim3(CS_THREADS), 0, s, gp, M, N, ldg, rows_per_split, dst);
+    if (splits > 1)
+        hipLaunchKernelGGL(col_sum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, partials, N, splits,
+                           out);
     return hipGetLastError();
 }
 

@@ -16,7 +16,12 @@ constexpr int64_t WS_SLOT_BYTES = 256;
 constexpr int64_t WS_SLOT_QA = 0;      // quantize of x / A
 constexpr int64_t WS_SLOT_QB = 1;      // quantize of w / B (linear_forward)
 constexpr int64_t WS_SLOT_GEMM = 2;    // GEMM output amax
-constexpr int64_t WS_BYTES = 4 * WS_SLOT_BYTES;
+constexpr int64_t WS_COUNTER_BYTES = 4 * WS_SLOT_BYTES;   // zeroed once, left zeroed by every call
+// Partial column sums of grad_bias (no zeroing needed: fully overwritten).
+constexpr int64_t WS_PART_BYTES = (int64_t)1 << 20;
+constexpr int64_t WS_BYTES = WS_COUNTER_BYTES + WS_PART_BYTES;
+
+inline float *ws_partials(void *ws) { return reinterpret_cast<float *>(static_cast<char *>(ws) + WS_COUNTER_BYTES); }
 
 inline uint32_t *ws_slot(void *ws, int64_t slot)
 {
@@ -52,9 +57,35 @@ struct QzParams {
 };
 
 hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s);
-// grad_bias: out[n] = sum_m g[m, n] for BF16 g [M, N] (leading dimension ldg).
-hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, hipStream_t s);
+// grad_bias: out[n] = sum_m g[m, n] for BF16 g [M, N] (leading dimension ldg);
+// partials: WS_PART_BYTES of scratch (the workspace's partial area).
+hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, float *partials,
+                               hipStream_t s);
 hipError_t launch_ws_zero(void *ws, int64_t bytes, hipStream_t s);
+
+// Unsigned division by a divisor d fixed for a launch, as a multiply-high
+// and a shift (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994, section 4): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l for every
+// n < 2^32 (the sum is formed in 64 bits, so it cannot overflow).  d = 0
+// stands for "one scale": the quotient is 0.
+struct GroupDiv {
+    uint32_t d, m;
+    int l;
+    __host__ __device__ void init(int64_t div)
+    {
+        d = (uint32_t)div;
+        l = 0;
+        while (l < 32 && ((uint64_t)1 << l) < (uint64_t)d) ++l;
+        m = d ? (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1) : 0;
+    }
+    __host__ __device__ uint32_t operator()(uint32_t n) const
+    {
+        if (d == 0) return 0;
+        const uint64_t t = ((uint64_t)n * m) >> 32;
+        return (uint32_t)((t + n) >> l);
+    }
+};
 
 struct GemmParams {
     const uint8_t *a, *b;
@@ -62,6 +93,7 @@ struct GemmParams {
     int64_t M, N, K;
     const float *sa, *sb;
     int64_t sa_group, sb_group;     // rows per scale: 0 (one scale), 1 (per row), G (row groups)
+    GroupDiv sa_div, sb_div;        // the same divisions (launch_qgemm fills them)
     // Batched products (grid y = batch index z): item z reads a + z*stride_a,
     // b + z*stride_b and writes out + z*stride_out (elements); its scale
     // rows are z*M + m and z*N + n of the flattened batch.
@@ -84,6 +116,14 @@ struct GemmParams {
     int fast;                       // branch-free buffer-load staging applies
     int tiles_m, tiles_n;
 };
+
+// Fills sa_div / sb_div from sa_group / sb_group; scale rows (z*M + m and
+// z*N + n) must stay below 2^32.
+inline void finish_groups(GemmParams &p)
+{
+    p.sa_div.init(p.sa_group);
+    p.sb_div.init(p.sb_group);
+}
 
 // a_fmt / b_fmt: FMT_*; a_mn / b_mn: operand stored MN-major.
 hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s);

@@ -62,6 +62,39 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int i)
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Byte transpose of a 4 x 4 block: row j is word r[j] (byte b = column b);
+// c[b] collects column b, row j in byte j.  Two rounds of v_perm_b32, whose
+// selector byte i picks byte i of the result from the 8 bytes {hi : lo}
+// (0..3 = lo's bytes, 4..7 = hi's).
+__device__ __forceinline__ void transpose_4x4_bytes(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                                    uint32_t (&c)[4])
+{
+    const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x06020400u);   // r0.0 r1.0 r0.2 r1.2
+    const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030501u);   // r0.1 r1.1 r0.3 r1.3
+    const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x06020400u);   // r2.0 r3.0 r2.2 r3.2
+    const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030501u);   // r2.1 r3.1 r2.3 r3.3
+    c[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+    c[1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+    c[2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+    c[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// 8 k-rows x 16 mn-bytes (r[j] = k-row j) -> 16 mn-rows of 8 k-bytes:
+// lo[e] holds k-rows 0..3 of mn-row e, hi[e] k-rows 4..7.
+__device__ __forceinline__ void transpose_8x16_bytes(const uint4 (&r)[8], uint32_t (&lo)[16], uint32_t (&hi)[16])
+{
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t c[4];
+        transpose_4x4_bytes(word_of(r[0], w), word_of(r[1], w), word_of(r[2], w), word_of(r[3], w), c);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lo[4 * w + b] = c[b];
+        transpose_4x4_bytes(word_of(r[4], w), word_of(r[5], w), word_of(r[6], w), word_of(r[7], w), c);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hi[4 * w + b] = c[b];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Stage one K step of one operand ([ROWS, 128 bytes] of the logical [MN, K]
 // matrix) from global memory into registers, then into LDS.
@@ -133,17 +166,12 @@ template <int ROWS> struct Stage<ROWS, true> {
             const int u = i * GEMM_THREADS + (int)threadIdx.x;
             if (u >= UNITS) continue;
             const int mg = u % GROUPS, kq = u / GROUPS;
+            uint32_t lo[16], hi[16];
+            transpose_8x16_bytes(r[i], lo, hi);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int w = e >> 2, sh = (e & 3) * 8;
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    lo |= ((word_of(r[i][j], w) >> sh) & 0xFFu) << (8 * j);
-                    hi |= ((word_of(r[i][j + 4], w) >> sh) & 0xFFu) << (8 * j);
-                }
                 const int row = mg * 16 + e;
-                *reinterpret_cast<uint2 *>(lds + lds_off(row, kq >> 1) + (kq & 1) * 8) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2 *>(lds + lds_off(row, kq >> 1) + (kq & 1) * 8) = make_uint2(lo[e], hi[e]);
             }
         }
     }
@@ -248,16 +276,12 @@ template <int ROWS> struct FastStage<ROWS, true> {
             const int u = i * GEMM_THREADS + (int)threadIdx.x;
             if (u >= UNITS) continue;
             const int mg = u % GROUPS, kq = u / GROUPS;
+            uint32_t lo[16], hi[16];
+            transpose_8x16_bytes(r[i], lo, hi);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int w = e >> 2, sh = (e & 3) * 8;
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    lo |= ((word_of(r[i][j], w) >> sh) & 0xFFu) << (8 * j);
-                    hi |= ((word_of(r[i][j + 4], w) >> sh) & 0xFFu) << (8 * j);
-                }
-                *reinterpret_cast<uint2 *>(lds + lds_off(mg * 16 + e, kq >> 1) + (kq & 1) * 8) = make_uint2(lo, hi);
+                const int row = mg * 16 + e;
+                *reinterpret_cast<uint2 *>(lds + lds_off(row, kq >> 1) + (kq & 1) * 8) = make_uint2(lo[e], hi[e]);
             }
         }
     }
@@ -359,12 +383,12 @@ struct Epilogue {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e])) * s_ab;
         } else {
-            const float s_row = p.sa[p.sa_group ? (p.row_base + row) / p.sa_group : 0];
+            const float s_row = p.sa[p.sa_div((uint32_t)(p.row_base + row))];
+            const uint32_t c0 = (uint32_t)(p.col_base + col);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t c = col + (e < n ? e : 0);
                 const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
-                v[e] = a * s_row * p.sb[p.sb_group ? (p.col_base + c) / p.sb_group : 0];
+                v[e] = a * s_row * p.sb[p.sb_div(c0 + (uint32_t)(e < n ? e : 0))];
             }
         }
         if (p.bias_dt >= 0) {
@@ -543,8 +567,10 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
     return hipGetLastError();
 }
 
-// Tile size: 256 x 256 when that still gives at least two tiles per CU,
-// else 128 x 128.  p.fast selects the branch-free buffer-load staging.
+// Tile size (general kernel): 256 x 256 when that still gives at least two
+// tiles per CU, else the largest of 128 x 128, 128 x 64 and 64 x 64 that
+// gives one per CU (unaligned operands: 128 x 128).  p.fast selects the
+// branch-free buffer-load staging.
 template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
 
 template <int AF, int BF, bool A_MN, bool B_MN>
@@ -558,8 +584,15 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
     if constexpr (AF != FMT_INT8)
         if (p.fast && !A_MN && !B_MN && big >= 256 && p.batch <= 1) return launch_nt<AF, BF>(p, s);
     if (p.fast) {
-        if (big >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
-        return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);
+        // The largest tile that still gives every CU a workgroup (batch
+        // items count: they are grid rows).
+        const int64_t nb = p.batch > 1 ? p.batch : 1;
+        const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
+        const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
+        if (big * nb >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
+        if (t128 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);
+        if (t128x64 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 64, 2, true>(p, s);
+        return launch_tile<AF, BF, A_MN, B_MN, 64, 64, 2, true>(p, s);
     }
     return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false>(p, s);
 }

@@ -22,8 +22,10 @@ hipError_t launch_qgemm_e5m2_e4m3(const GemmParams &p, int a_mn, int b_mn, hipSt
 hipError_t launch_qgemm_e5m2_e5m2(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
 hipError_t launch_qgemm_int8_int8(const GemmParams &p, int a_mn, int b_mn, hipStream_t s);
 
-hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s)
+hipError_t launch_qgemm(const GemmParams &pp, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s)
 {
+    GemmParams p = pp;
+    finish_groups(p);
     if (a_fmt == FMT_INT8) return launch_qgemm_int8_int8(p, a_mn, b_mn, s);
     if (a_fmt == FMT_E4M3) return b_fmt == FMT_E4M3 ? launch_qgemm_e4m3_e4m3(p, a_mn, b_mn, s)
                                                     : launch_qgemm_e4m3_e5m2(p, a_mn, b_mn, s);
@@ -179,6 +181,8 @@ ql_status check_gemm(const GemmArgs &g)
     if (g.out_dt == QL_DT_E4M3 && !g.out_scale)
         return fail(QL_ERR_NULL, "qgemm: E4M3 output requires out_scale (the output quantization step)");
     if (g.out_amax && !g.ws) return fail(QL_ERR_NULL, "qgemm: out_amax needs a workspace");
+    if ((g.sa_gran == QL_PER_ROW && g.M >= ((int64_t)1 << 32)) || (g.sb_gran == QL_PER_ROW && g.N >= ((int64_t)1 << 32)))
+        return fail(QL_ERR_UNSUPPORTED, "qgemm: per-row scales support fewer than 2^32 rows");
     const int64_t bm = 128;
     if (((g.M + bm - 1) / bm) * ((g.N + bm - 1) / bm) > 0x7FFFFFFF)
         return fail(QL_ERR_UNSUPPORTED, "qgemm: output too large for one launch");
@@ -236,7 +240,8 @@ ql_status ql_workspace_init(void *ws, size_t bytes, void *stream)
     if (!ws) return fail(QL_ERR_NULL, "workspace_init: ws is NULL");
     if (bytes < (size_t)ql::WS_BYTES)
         return fail(QL_ERR_VALUE, "workspace_init: %zu bytes given, %lld needed", bytes, (long long)ql::WS_BYTES);
-    return hip_status(ql::launch_ws_zero(ws, ql::WS_BYTES, static_cast<hipStream_t>(stream)), "workspace_init");
+    return hip_status(ql::launch_ws_zero(ws, ql::WS_COUNTER_BYTES, static_cast<hipStream_t>(stream)),
+                      "workspace_init");
 }
 
 ql_status ql_quantize(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
@@ -362,6 +367,8 @@ ql_status ql_qgemm_batched(const void *a_q, ql_qfmt a_fmt, ql_layout a_lay, int6
         return fail(QL_ERR_VALUE, "qgemm_batched: negative scale group size");
     if (stride_a < 0 || stride_b < 0 || stride_out < 0)
         return fail(QL_ERR_VALUE, "qgemm_batched: negative batch stride");
+    if (batch * M >= ((int64_t)1 << 32) || batch * N >= ((int64_t)1 << 32))
+        return fail(QL_ERR_UNSUPPORTED, "qgemm_batched: batch*M and batch*N must stay below 2^32");
     // Each item is checked as one product; the scale granularity is checked
     // through the group sizes above.
     GemmArgs g{a_q, a_fmt, a_lay, lda, b_q, b_fmt, b_lay, ldb, M, N, K, sa, QL_PER_TENSOR, sb, QL_PER_TENSOR,
@@ -445,6 +452,7 @@ ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
         if (M < 0 || N < 0) return fail(QL_ERR_VALUE, "linear_backward: negative size");
         if (!dbias && N > 0) return fail(QL_ERR_NULL, "linear_backward: dbias is required by the mask");
         if (!g && M > 0 && N > 0) return fail(QL_ERR_NULL, "linear_backward: g is required");
+        if (!ws && N > 0) return fail(QL_ERR_NULL, "linear_backward: grad_bias needs a workspace");
     }
     const bool gemms = want_dx || want_dw;
     GemmArgs gx{}, gw{};
@@ -485,7 +493,7 @@ ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
         }
     }
     if (want_db && M >= 0 && N > 0) {
-        hipError_t e = ql::launch_col_sum_bf16(g, M, N, N, dbias, s);
+        hipError_t e = ql::launch_col_sum_bf16(g, M, N, N, dbias, ql::ws_partials(ws), s);
         if (e != hipSuccess) return hip_status(e, "linear_backward: grad_bias");
     }
     return QL_OK;

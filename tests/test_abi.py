@@ -193,6 +193,7 @@ def _bwd(**kw):
     (dict(x_fmt=5), _lib.QL_ERR_VALUE),
     (dict(K=-1), _lib.QL_ERR_VALUE),
     (dict(masks=4, dbias=None), _lib.QL_ERR_NULL),
+    (dict(masks=4, ws=None), _lib.QL_ERR_NULL),     # grad_bias's partial sums live in the workspace
     (dict(sg=None), _lib.QL_ERR_NULL),
     (dict(g_q=None), _lib.QL_ERR_NULL),
     (dict(ws=None), _lib.QL_ERR_NULL),

@@ -76,8 +76,10 @@ def test_linear_forward_delayed_fp8_out_and_int8(orc):
 
 
 def _dbias_bound(g_vals, M):
-    """FP32 column sums in a fixed order of M/16 + 16 additions."""
-    n = M // 16 + 17
+    """FP32 column sums in a fixed order: a column's sum passes through at
+    most ceil(ceil(M/S)/4) + 3 + S additions for S <= 32 row splits, i.e.
+    fewer than M/4 + 40 (gamma_n bound of any such summation tree)."""
+    n = M // 4 + 40
     u = 2.0 ** -24
     return (n * u / (1 - n * u)) * np.abs(g_vals).sum(axis=0) + 1e-45
 
