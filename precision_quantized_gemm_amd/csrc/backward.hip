@@ -93,8 +93,13 @@ __global__ __launch_bounds__(256) void col_sum_final(const float *part, int64_t 
 {
     const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (col >= N) return;
-    float t = part[col];
-    for (int s = 1; s < splits; ++s) t += part[(int64_t)s * N + col];
+    float v[CS_MAX_SPLITS];                        // every load in flight, then added in split order
+#pragma unroll
+    for (int s = 0; s < CS_MAX_SPLITS; ++s) v[s] = s < splits ? part[(int64_t)s * N + col] : 0.0f;
+    float t = v[0];
+#pragma unroll
+    for (int s = 1; s < CS_MAX_SPLITS; ++s)
+        if (s < splits) t += v[s];
     out[col] = t;
 }
 

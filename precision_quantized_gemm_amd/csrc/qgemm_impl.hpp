@@ -1,4 +1,5 @@
-// qgemm_impl.hpp -- scaled FP8 / INT8 matrix-core GEMM for gfx950.
+// qgemm_impl.hpp -- the general scaled FP8 / INT8 matrix-core GEMM kernel
+// for gfx950 (every layout and alignment), and the per-shape dispatch.
 //
 //   out[m, n] = (sum_k A[m, k] * B[n, k]) * sa[m|0] * sb[n|0] (+ bias[n])
 //
@@ -9,8 +10,8 @@
 //
 // Design (one workgroup = 4 waves = one BM x BN output tile):
 //   * K advances in steps of 128 bytes.  Each step's A and B tiles are
-//     staged in LDS, double buffered: the global loads of step k+1 are in
-//     flight while the matrix cores work on step k.
+//     staged in LDS, double buffered, from two register sets: the global
+//     loads of step k+2 are in flight while the matrix cores work on step k.
 //   * LDS holds every operand K-major (128 bytes per row) with a 16-byte
 //     chunk swizzle, so the fragment reads (one row per lane, two 16-byte
 //     chunks) are free of bank conflicts.  MN-major operands are transposed
@@ -29,21 +30,13 @@
 //     quantize reduction).
 #pragma once
 
-#include "qdev.hpp"
-#include "internal.hpp"
+#include "qgemm_common.hpp"
 
 #include <type_traits>
 
 namespace ql {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int GEMM_BK = 128;
-constexpr int GEMM_THREADS = 256;
-constexpr int GEMM_GM = 8;   // tile-rows per group in the tile order
-
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 7); }
 __device__ __forceinline__ int lds_off(int r, int chunk) { return r * GEMM_BK + ((chunk ^ lds_swz(r)) << 4); }
 
@@ -186,12 +179,8 @@ template <int ROWS> struct Stage<ROWS, true> {
 // is needed per load.  Chunks past K (the last K step) get an offset far
 // outside the range.  Needs 16-byte aligned operands, leading dimensions and
 // K (K-major) or MN extent (MN-major) that are multiples of 16, and byte
-// offsets below 2^31 (checked on the host).
-constexpr uint32_t BUF_OOB = 0x80000000u;
-constexpr int BUF_WORD3 = 0x00020000;   // gfx9 raw-buffer descriptor word 3
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
+// offsets below 2^31 (checked on the host).  BUF_OOB / BUF_WORD3 are in
+// qgemm_common.hpp.
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -336,110 +325,7 @@ __device__ __forceinline__ v8i load_frag(const uint8_t *lds, int row, int g)
     return f;
 }
 
-// Fused epilogue for 4 consecutive outputs of one row:
-//   v = acc * sa[row|0] * sb[col|0] (+ bias[col]), then the output cast.
-// Per-tensor scales fold into one FP32 product sa*sb (either order of the
-// two multiplies is within the float acceptance bound).  E4M3 output
-// multiplies by RN(1/out_scale): its result differs from the correctly
-// rounded quotient by at most one FP32 rounding, which the FP8 acceptance
-// set allows for.
-struct Epilogue {
-    const GemmParams &p;
-    float inv_os;       // RN(1 / out_scale) for E4M3 output
-    float s_ab;         // sa[0] * sb[0] when both are per tensor
-    bool per_tensor;
-    __device__ __forceinline__ explicit Epilogue(const GemmParams &pp) : p(pp)
-    {
-        inv_os = pp.out_dt == DT_E4M3 ? 1.0f / pp.out_scale[0] : 1.0f;
-        per_tensor = pp.sa_group == 0 && pp.sb_group == 0;
-        s_ab = (per_tensor && pp.out_dt != DT_INT32) ? pp.sa[0] * pp.sb[0] : 1.0f;
-    }
-
-    __device__ __forceinline__ float bias_at(int64_t col) const
-    {
-        if (p.bias_dt == DT_FP32) return static_cast<const float *>(p.bias)[col];
-        if (p.bias_dt == DT_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p.bias)[col] << 16);
-        if (p.bias_dt == BIAS_Q_E4M3)
-            return fp8_decode<FMT_E4M3>(static_cast<const uint8_t *>(p.bias)[col]) * p.bias_scale[0];
-        if (p.bias_dt == BIAS_Q_E5M2)
-            return fp8_decode<FMT_E5M2>(static_cast<const uint8_t *>(p.bias)[col]) * p.bias_scale[0];
-        return 0.0f;
-    }
-
-    template <bool INT_ACC>
-    __device__ __forceinline__ uint32_t store4(uint4 w, int64_t row, int64_t col, uint32_t vmax) const
-    {
-        const uint32_t raw[4] = {w.x, w.y, w.z, w.w};
-        const int n = p.N - col < 4 ? (int)(p.N - col) : 4;
-        const int64_t o = row * p.ldo + col;
-        if (p.out_dt == DT_INT32) {
-            int32_t *out = static_cast<int32_t *>(p.out) + o;
-            if (n == 4 && p.out_vec4) *reinterpret_cast<uint4 *>(out) = w;
-            else for (int e = 0; e < n; ++e) out[e] = (int32_t)raw[e];
-            return vmax;
-        }
-        float v[4];
-        if (per_tensor) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e])) * s_ab;
-        } else {
-            const float s_row = p.sa[p.sa_div((uint32_t)(p.row_base + row))];
-            const uint32_t c0 = (uint32_t)(p.col_base + col);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e]);
-                v[e] = a * s_row * p.sb[p.sb_div(c0 + (uint32_t)(e < n ? e : 0))];
-            }
-        }
-        if (p.bias_dt >= 0) {
-            if (n == 4 && p.bias_dt == DT_FP32 && (col & 3) == 0 && p.out_vec4) {
-                const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.bias) + col);
-                v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bias_at(col + (e < n ? e : 0));
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (e < n) { const uint32_t b = absbits_f32(v[e]); vmax = b > vmax ? b : vmax; }
-        if (p.out_dt == DT_BF16) {
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-            uint16_t *out = static_cast<uint16_t *>(p.out) + o;
-            if (n == 4 && p.out_vec4)
-                *reinterpret_cast<uint2 *>(out) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-            else for (int e = 0; e < n; ++e) out[e] = h[e];
-        } else if (p.out_dt == DT_FP32) {
-            float *out = static_cast<float *>(p.out) + o;
-            if (n == 4 && p.out_vec4) *reinterpret_cast<float4 *>(out) = make_float4(v[0], v[1], v[2], v[3]);
-            else for (int e = 0; e < n; ++e) out[e] = v[e];
-        } else {
-            const uint32_t c = encode4<FMT_E4M3>(v[0] * inv_os, v[1] * inv_os, v[2] * inv_os, v[3] * inv_os);
-            uint8_t *out = static_cast<uint8_t *>(p.out) + o;
-            if (n == 4 && p.out_vec4) *reinterpret_cast<uint32_t *>(out) = c;
-            else for (int e = 0; e < n; ++e) out[e] = (uint8_t)(c >> (8 * e));
-        }
-        return vmax;
-    }
-};
-
-// Linear workgroup id -> (tile_m, tile_n): XCD-contiguous, then grouped.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn)
-{
-    const int total = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-    const int per_group = GEMM_GM * tiles_n;
-    const int first_m = (t / per_group) * GEMM_GM;
-    const int gsize = tiles_m - first_m < GEMM_GM ? tiles_m - first_m : GEMM_GM;
-    const int in_group = t - (t / per_group) * per_group;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST>
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST, int PF>
 __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 {
     typedef Mma<AF, BF> MMA;
@@ -474,27 +360,39 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 
     typedef typename std::conditional<FAST, FastStage<BM, A_MN>, SafeStage<BM, A_MN> >::type StageA;
     typedef typename std::conditional<FAST, FastStage<BN, B_MN>, SafeStage<BN, B_MN> >::type StageB;
-    StageA sa_stage;
-    StageB sb_stage;
-    sa_stage.init(p.a, p.lda, m0, p.M, p.K);
-    sb_stage.init(p.b, p.ldb, n0, p.N, p.K);
-    if constexpr (!FAST) { sa_stage.aligned = p.a_aligned; sb_stage.aligned = p.b_aligned; }
+    // PF = 2: two register sets per operand, so the global loads of step
+    // k+2 are issued while step k is computed and step k+1 goes from
+    // registers to LDS (each load has two steps to arrive).  PF = 1: one set,
+    // step k+1's loads overlap step k.  Loads past K read zeros (bounds
+    // checks, or offsets outside the buffer range).
+    static_assert(PF == 1 || PF == 2, "prefetch depth");
+    StageA sa0, sa1;
+    StageB sb0, sb1;
+    sa0.init(p.a, p.lda, m0, p.M, p.K);
+    sb0.init(p.b, p.ldb, n0, p.N, p.K);
+    if constexpr (!FAST) { sa0.aligned = p.a_aligned; sb0.aligned = p.b_aligned; }
+    if constexpr (PF == 2) { sa1 = sa0; sb1 = sb0; }
     const int nk = (int)((p.K + GEMM_BK - 1) / GEMM_BK);
     if (nk > 0) {
-        sa_stage.load(0, p.K);
-        sb_stage.load(0, p.K);
-        sa_stage.store(lds);
-        sb_stage.store(lds + BM * GEMM_BK);
+        sa0.load(0, p.K);
+        sb0.load(0, p.K);
+        if constexpr (PF == 2) {
+            sa1.load(GEMM_BK, p.K);
+            sb1.load(GEMM_BK, p.K);
+        }
+        sa0.store(lds);
+        sb0.store(lds + BM * GEMM_BK);
     }
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
+    // Step kt: reload set r with step kt + PF, compute step kt from LDS,
+    // store set n (step kt + 1) into the other LDS buffer.
+    auto step = [&](int kt, StageA &ra, StageB &rb, StageA &na, StageB &nb) {
         uint8_t *cur = lds + (kt & 1) * STAGE;
         uint8_t *nxt = lds + ((kt + 1) & 1) * STAGE;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int64_t k0 = (int64_t)(kt + 1) * GEMM_BK;
-            sa_stage.load(k0, p.K);
-            sb_stage.load(k0, p.K);
+        const int64_t kn = (int64_t)(kt + PF) * GEMM_BK;
+        if (PF == 2 || kt + 1 < nk) {
+            ra.load(kn, p.K);
+            rb.load(kn, p.K);
         }
         const uint8_t *as = cur, *bs = cur + BM * GEMM_BK;
         v8i af[TM];
@@ -506,11 +404,19 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 #pragma unroll
             for (int i = 0; i < TM; ++i) MMA::run(acc[i][j], af[i], bf);
         }
-        if (more) {
-            sa_stage.store(nxt);
-            sb_stage.store(nxt + BM * GEMM_BK);
+        if (kt + 1 < nk) {
+            na.store(nxt);
+            nb.store(nxt + BM * GEMM_BK);
         }
         __syncthreads();
+    };
+    if constexpr (PF == 2) {
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, sa0, sb0, sa1, sb1);
+            if (kt + 1 < nk) step(kt + 1, sa1, sb1, sa0, sb0);
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) step(kt, sa0, sb0, sa0, sb0);
     }
 
     // Epilogue, one 16-row slab of the wave tile at a time: the slab's
@@ -549,7 +455,7 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
     }
 }
 
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST>
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST, int PF>
 hipError_t launch_tile(GemmParams p, hipStream_t s)
 {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -562,7 +468,7 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
     }
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
-    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST>), dim3((unsigned)grid, batch),
+    hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST, PF>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
     return hipGetLastError();
 }
@@ -589,12 +495,12 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         const int64_t nb = p.batch > 1 ? p.batch : 1;
         const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
         const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
-        if (big * nb >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true>(p, s);
-        if (t128 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, true>(p, s);
-        if (t128x64 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 64, 2, true>(p, s);
-        return launch_tile<AF, BF, A_MN, B_MN, 64, 64, 2, true>(p, s);
+        if (big * nb >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true, 1>(p, s);
+        if (t128 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 1, true, 2>(p, s);
+        if (t128x64 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 64, 2, true, 2>(p, s);
+        return launch_tile<AF, BF, A_MN, B_MN, 64, 64, 2, true, 2>(p, s);
     }
-    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false>(p, s);
+    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false, 1>(p, s);
 }
 
 template <int AF, int BF>

@@ -38,7 +38,7 @@
 // LDS with 16-byte writes.
 #pragma once
 
-#include "qgemm_impl.hpp"
+#include "qgemm_common.hpp"
 
 namespace ql {
 

@@ -297,19 +297,37 @@ __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
         ustep = w;
         if (tr >= rpp) tr = r1 - r0;                // idle threads
     }
+    // A thread walks its items (r, u) in order, QZ_UNROLL at a time so that
+    // their loads are all in flight together.
+    auto next = [&](int64_t &r, int64_t &u) {
+        u += ustep;
+        if (u >= W) { u = tu; r += rpp; }
+    };
     uint32_t m = 0;
-    for (int64_t r = r0 + tr; r < r1; r += rpp) {
-        const T *x = static_cast<const T *>(p.x) + r * p.ldx;
-        for (int64_t u = tu; u < W; u += ustep) {
-            uint32_t t;
-            if (VEC) {
-                Vec16<T> v;
-                v.load(x + u * QZ_UNIT);
-                t = v.amax_bits();
-            } else {
-                t = absbits_f32(load1<T>(x, u));
-            }
-            m = t > m ? t : m;
+    for (int64_t r = r0 + tr, u = tu; r < r1 && u < W;) {
+        int64_t rr[QZ_UNROLL], uu[QZ_UNROLL];
+        bool ok[QZ_UNROLL];
+#pragma unroll
+        for (int k = 0; k < QZ_UNROLL; ++k) {
+            ok[k] = r < r1;
+            rr[k] = r; uu[k] = u;
+            if (ok[k]) next(r, u);
+        }
+        if (VEC) {
+            Vec16<T> v[QZ_UNROLL];
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                if (ok[k]) v[k].load(static_cast<const T *>(p.x) + rr[k] * p.ldx + uu[k] * QZ_UNIT);
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                if (ok[k]) { const uint32_t t = v[k].amax_bits(); m = t > m ? t : m; }
+        } else {
+            float v[QZ_UNROLL];
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                v[k] = ok[k] ? load1<T>(static_cast<const T *>(p.x) + rr[k] * p.ldx, uu[k]) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k) { const uint32_t t = absbits_f32(v[k]); m = t > m ? t : m; }
         }
     }
     __shared__ uint32_t red[QZ_ROW_THREADS / 64];
@@ -322,17 +340,33 @@ __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
         if (p.scale_out) p.scale_out[grp] = step;
     }
     const Divider div(DELAYED ? p.scale_src[grp] : step);
-    for (int64_t r = r0 + tr; r < r1; r += rpp) {
-        const T *x = static_cast<const T *>(p.x) + r * p.ldx;
-        uint8_t *xq = static_cast<uint8_t *>(p.xq) + r * p.ldq;
-        for (int64_t u = tu; u < W; u += ustep) {
-            if (VEC) {
-                Vec16<T> v;
-                v.load(x + u * QZ_UNIT);
-                *reinterpret_cast<uint4 *>(xq + u * QZ_UNIT) = encode16<FMT>(v, div);
-            } else {
-                xq[u] = encode1<FMT>(div(load1<T>(x, u)));
-            }
+    for (int64_t r = r0 + tr, u = tu; r < r1 && u < W;) {
+        int64_t rr[QZ_UNROLL], uu[QZ_UNROLL];
+        bool ok[QZ_UNROLL];
+#pragma unroll
+        for (int k = 0; k < QZ_UNROLL; ++k) {
+            ok[k] = r < r1;
+            rr[k] = r; uu[k] = u;
+            if (ok[k]) next(r, u);
+        }
+        if (VEC) {
+            Vec16<T> v[QZ_UNROLL];
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                if (ok[k]) v[k].load(static_cast<const T *>(p.x) + rr[k] * p.ldx + uu[k] * QZ_UNIT);
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                if (ok[k])
+                    *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.xq) + rr[k] * p.ldq + uu[k] * QZ_UNIT) =
+                        encode16<FMT>(v[k], div);
+        } else {
+            float v[QZ_UNROLL];
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                v[k] = ok[k] ? load1<T>(static_cast<const T *>(p.x) + rr[k] * p.ldx, uu[k]) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < QZ_UNROLL; ++k)
+                if (ok[k]) static_cast<uint8_t *>(p.xq)[rr[k] * p.ldq + uu[k]] = encode1<FMT>(div(v[k]));
         }
     }
 }
