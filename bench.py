@@ -189,6 +189,45 @@ def time_per_head(torch, q, _lib, synth, dev, reps):
             "note": "launch-bound sizes (tens of MFLOP per product)"}
 
 
+SCLK_FILES = sorted(Path("/sys/class/drm").glob("card*/device/pp_dpm_sclk")) if Path("/sys/class/drm").exists() else []
+
+
+def read_sclk_mhz():
+    """The current shader clock (the level marked '*' in pp_dpm_sclk), or
+    None where the file is not readable."""
+    for f in SCLK_FILES:
+        try:
+            for line in f.read_text().splitlines():
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def sclk_under(fn, torch, launches):
+    """Average shader clock (MHz) sampled every 2 ms while `launches` calls
+    of fn run back to back on the GPU (all enqueued first), or None."""
+    if read_sclk_mhz() is None:
+        return None
+    torch.cuda.synchronize()
+    done = torch.cuda.Event()
+    for _ in range(launches):
+        fn()
+    done.record()
+    samples = []
+    while not done.query():
+        v = read_sclk_mhz()
+        if v is not None:
+            samples.append(v)
+        time.sleep(0.002)
+    torch.cuda.synchronize()
+    # Drop the first and last tenth (ramp and drain).
+    k = len(samples) // 10
+    core = samples[k:len(samples) - k] if len(samples) > 10 else samples
+    return round(sum(core) / len(core), 1) if core else None
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -306,6 +345,8 @@ def main():
     ms_qa = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
     ms_qb = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
     ms_gemm = sum(ev[2].elapsed_time(ev[3]) for ev in events) / args.steps
+    gemm_each = sorted(ev[2].elapsed_time(ev[3]) for ev in events)
+    pct = lambda f: gemm_each[min(len(gemm_each) - 1, int(f * len(gemm_each)))]
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
@@ -363,6 +404,9 @@ def main():
     log("per-head batched products")
     per_head = time_per_head(torch, q, _lib, synth, dev, args.steps)
 
+    log("shader clock under the GEMM")
+    sclk = sclk_under(gemm, torch, 500)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -396,6 +440,9 @@ def main():
             "traffic": gemm_traffic(),
             "kernel": "qgemm_nt_kernel<E4M3,E4M3> (256x256x128 tiles)",
             "ms_per_launch": round(ms_gemm, 5),
+            "ms_per_launch_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+            "sclk_mhz_under_gemm": sclk,
+            "frac_at_measured_sclk": None if not sclk else round(gemm_tflops / (PEAK_FP8_TFLOPS * sclk / 2400.0), 4),
             "per_launch_flops": flops,
         },
         "quantize": {
