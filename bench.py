@@ -42,9 +42,10 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak
 # already scaled by the copy calibration, with the hash of the kernel
 # sources they were taken on; used only while the sources still match.
 TRAFFIC_FILE = ROOT / "profiles" / "qgemm_nt_e4m3_large_fp8_traffic.json"
-# The sources the pipelined E4M3 kernel is compiled from (the general kernel
-# in qgemm_impl.hpp does not enter its code).
-KERNEL_SOURCES = ["qgemm_nt.hpp", "qgemm_common.hpp", "qdev.hpp", "internal.hpp", "qgemm_e4m3_e4m3.hip"]
+# The sources the pipelined E4M3 kernel is compiled from (the general and
+# direct-to-LDS kernels in qgemm_impl.hpp / qgemm_dl.hpp, instantiated in the
+# same unit, do not enter its code).
+KERNEL_SOURCES = ["qgemm_nt.hpp", "qgemm_common.hpp", "qdev.hpp", "internal.hpp"]
 
 
 def parse():

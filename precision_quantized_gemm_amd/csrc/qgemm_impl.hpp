@@ -325,6 +325,62 @@ __device__ __forceinline__ v8i load_frag(const uint8_t *lds, int row, int g)
     return f;
 }
 
+// Batch item z (grid y): its operands, its output and its scale rows.
+__device__ __forceinline__ void select_batch_item(GemmParams &p)
+{
+    const int64_t z = blockIdx.y;
+    const int eb = p.out_dt == DT_BF16 ? 2 : p.out_dt == DT_E4M3 ? 1 : 4;
+    p.a += z * p.stride_a;
+    p.b += z * p.stride_b;
+    p.out = static_cast<char *>(p.out) + z * p.stride_out * eb;
+    p.row_base = z * p.M;
+    p.col_base = z * p.N;
+}
+
+// Epilogue of a wave's TM x TN grid of 16 x 16 accumulators (16x16x128
+// layout: element r of lane (lr, g) is row 4g + r, column lr), one 16-row
+// slab at a time: the slab goes to a per-wave LDS area (raw FP32 / INT32
+// bits), then each lane takes 4 consecutive columns of a row, so stores are
+// contiguous along rows.  Reuses `lds` (every wave must be done with it),
+// and ends with the optional out_amax election.
+template <typename MMA, int TM, int TN, int WN>
+__device__ __forceinline__ void epilogue_tile(const GemmParams &p, uint8_t *lds, uint32_t *red,
+                                              typename MMA::acc_t (&acc)[TM][TN], int64_t row0, int64_t col0,
+                                              int wave, int lane)
+{
+    const int lr = lane & 15, g = lane >> 4;
+    constexpr int EP_LD = WN + 4;                       // padded row, in words
+    uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 16 * EP_LD;
+    Epilogue epi(p);
+    uint32_t vmax = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ep[(g * 4 + r) * EP_LD + j * 16 + lr] = MMA::bits(acc[i][j], r);
+        __syncthreads();
+        constexpr int C4 = WN / 4;                       // 4-column groups per row
+#pragma unroll 1
+        for (int idx = lane; idx < 16 * C4; idx += 64) {
+            const int rr = idx / C4, c4 = idx - rr * C4;
+            const uint4 w = *reinterpret_cast<const uint4 *>(ep + rr * EP_LD + c4 * 4);
+            const int64_t row = row0 + i * 16 + rr;
+            const int64_t col = col0 + c4 * 4;
+            if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w, row, col, vmax);
+        }
+    }
+    if (p.out_amax) {
+        vmax = block_max_u32(vmax, red);
+        if (threadIdx.x == 0) {
+            uint32_t bits;
+            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
+        }
+    }
+}
+
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST, int PF>
 __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
 {
@@ -335,16 +391,7 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
     __shared__ uint32_t red[GEMM_THREADS / 64];
 
-    // Batch item z (grid y): its operands, its output and its scale rows.
-    {
-        const int64_t z = blockIdx.y;
-        const int eb = p.out_dt == DT_BF16 ? 2 : p.out_dt == DT_E4M3 ? 1 : 4;
-        p.a += z * p.stride_a;
-        p.b += z * p.stride_b;
-        p.out = static_cast<char *>(p.out) + z * p.stride_out * eb;
-        p.row_base = z * p.M;
-        p.col_base = z * p.N;
-    }
+    select_batch_item(p);
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -419,40 +466,7 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_kernel(GemmParams p)
         for (int kt = 0; kt < nk; ++kt) step(kt, sa0, sb0, sa0, sb0);
     }
 
-    // Epilogue, one 16-row slab of the wave tile at a time: the slab's
-    // accumulators go to a per-wave LDS area (raw FP32 / INT32 bits), then
-    // each lane takes 4 consecutive columns of a row, so stores are
-    // contiguous along rows.
-    constexpr int EP_LD = WN + 4;                       // padded row, in words
-    uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 16 * EP_LD;
-    Epilogue epi(p);
-    uint32_t vmax = 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ep[(g * 4 + r) * EP_LD + j * 16 + lr] = MMA::bits(acc[i][j], r);
-        __syncthreads();
-        constexpr int C4 = WN / 4;                       // 4-column groups per row
-#pragma unroll 1
-        for (int idx = lane; idx < 16 * C4; idx += 64) {
-            const int rr = idx / C4, c4 = idx - rr * C4;
-            const uint4 w = *reinterpret_cast<const uint4 *>(ep + rr * EP_LD + c4 * 4);
-            const int64_t row = m0 + wm0 + i * 16 + rr;
-            const int64_t col = n0 + wn0 + c4 * 4;
-            if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w, row, col, vmax);
-        }
-    }
-    if (p.out_amax) {
-        vmax = block_max_u32(vmax, red);
-        if (threadIdx.x == 0) {
-            uint32_t bits;
-            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
-        }
-    }
+    epilogue_tile<MMA, TM, TN, WN>(p, lds, red, acc, m0 + wm0, n0 + wn0, wave, lane);
 }
 
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST, int PF>
@@ -478,6 +492,8 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
 // gives one per CU (unaligned operands: 128 x 128).  p.fast selects the
 // branch-free buffer-load staging.
 template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int STAGES, int MINW>
+hipError_t launch_dl(GemmParams p, hipStream_t s);
 
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)
@@ -489,6 +505,20 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
     // not fit its register budget.
     if constexpr (AF != FMT_INT8)
         if (p.fast && !A_MN && !B_MN && big >= 256 && p.batch <= 1) return launch_nt<AF, BF>(p, s);
+    if (p.fast && (A_MN || B_MN)) {
+        // An MN-major operand: the direct-to-LDS kernel (transpose reads).
+        // Tiles and ring depth keep two workgroups per CU where the grid
+        // allows it (measured on the 2048 x 4096 x 1024 backward products):
+        // 128x128 with 4 stages (128 KiB of LDS, one per CU) only when that
+        // still gives two tiles per CU, else 128x64 with 3 stages (72 KiB),
+        // else 64x64 with 4 stages (64 KiB).
+        const int64_t nb = p.batch > 1 ? p.batch : 1;
+        const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
+        const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
+        if (t128 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 128, 4, 1>(p, s);
+        if (t128x64 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 64, 3, 1>(p, s);
+        return launch_dl<AF, BF, A_MN, B_MN, 64, 64, 4, 2>(p, s);
+    }
     if (p.fast) {
         // The largest tile that still gives every CU a workgroup (batch
         // items count: they are grid rows).

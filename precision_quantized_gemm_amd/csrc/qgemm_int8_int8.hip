@@ -2,6 +2,7 @@
 // FMT_INT8 (one file per format pair so the build compiles them in parallel).
 #include "qgemm_impl.hpp"
 #include "qgemm_nt.hpp"
+#include "qgemm_dl.hpp"
 
 namespace ql {
 

@@ -357,3 +357,35 @@ def test_pipelined_fast_epilogue(orc, out_dtype, bias_kind, af, bf):
     else:
         print("fast epilogue", check_float(got, v, S, H, sasb, K, bias=bias_of(bias_vals, ns),
                                            what=f"fast epi {out_dtype}"))
+
+
+@pytest.mark.parametrize("al,bl", [(0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("shape", [(1040, 560, 1008), (2048, 1040, 384), (2064, 2048, 256), (64, 48, 16),
+                                   (16, 16, 2064)])
+@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (2, 2)])
+def test_direct_lds_mn_major(orc, al, bl, shape, af, bf):
+    """Aligned products with an MN-major operand take the direct-to-LDS
+    kernel (transpose reads): 64x64, 128x64 and 128x128 tiles, partial edge
+    tiles, a partial last k-step (K = 1008), a single 16-deep step and a
+    long K; sampled entries include the last rows and columns.  INT8
+    accumulators bit exact."""
+    M, N, K = shape
+    a = finite_codes(orc, 71, af * 3 + al, M, K, af)
+    b = finite_codes(orc, 72, bf * 3 + bl, N, K, bf)
+    rng = np.random.default_rng(73)
+    rows = np.unique(np.array([0, 15, 16, 63, 64, 127, 128, M - 1]).clip(0, M - 1))
+    cols = np.unique(np.array([0, 15, 16, 63, 64, 127, 128, N - 1]).clip(0, N - 1))
+    ms = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 3000)])
+    ns = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 3000)])
+    ms, ns = ms.astype(np.int64), ns.astype(np.int64)
+    a_st, b_st = storage(a, al), storage(b, bl)
+    if af == 2:
+        acc, S, iacc, H, v, sasb = oracle_entries(orc, a_st, 2, al, b_st, 2, bl, K, ms, ns, [1.0], 0, [1.0], 0, None)
+        out = run_gpu(a_st, 2, al, b_st, 2, bl, K, [1.0], 0, [1.0], 0, out_dtype="int32").numpy()
+        assert np.array_equal(out[ms, ns].astype(np.int64), iacc)
+        return
+    bias = synth.normal(74, 0, N, 0.5)
+    acc, S, _, H, v, sasb = oracle_entries(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, [0.004], 0, [0.5], 0, bias)
+    out = run_gpu(a_st, af, al, b_st, bf, bl, K, [0.004], 0, [0.5], 0, bias=bias, out_dtype="bf16")
+    print("direct-lds", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, bias=bias_of(bias, ns),
+                                    what=f"dl {shape} lay={al},{bl} fmt={af},{bf}"))
