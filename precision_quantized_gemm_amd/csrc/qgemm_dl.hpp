@@ -70,7 +70,10 @@ template <int R, bool MN> struct DlOperand {
             rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(base + row0 * ld), (short)0,
                                                      (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), BUF_WORD3);
         } else {
-            const int64_t bytes = K * ld - row0;        // k-rows >= K fall outside
+            // k-rows >= K fall outside.  A tile wholly past the MN extent
+            // (an empty operand, which may have no memory at all) reads
+            // nothing.
+            const int64_t bytes = row0 < rows_total ? K * ld - row0 : 0;
             rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(base + row0), (short)0,
                                                      (int)(bytes > 0 ? (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0),
                                                      BUF_WORD3);

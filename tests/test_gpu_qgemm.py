@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import precision_quantized_gemm_amd as q
-from precision_quantized_gemm_amd import synth
+from precision_quantized_gemm_amd import _lib, synth
 from tolerance import check_float, check_fp8_out
 
 pytestmark = pytest.mark.gpu
@@ -389,3 +389,37 @@ def test_direct_lds_mn_major(orc, al, bl, shape, af, bf):
     out = run_gpu(a_st, af, al, b_st, bf, bl, K, [0.004], 0, [0.5], 0, bias=bias, out_dtype="bf16")
     print("direct-lds", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, bias=bias_of(bias, ns),
                                     what=f"dl {shape} lay={al},{bl} fmt={af},{bf}"))
+
+
+def test_direct_lds_degenerate():
+    """MN-major operands on the direct-to-LDS path: K = 0 gives bias only;
+    M = 0 (with a leading dimension past the empty extent) and N = 0 write
+    nothing and publish out_amax = 0."""
+    dev = "cuda"
+    s1 = torch.ones(1, device=dev)
+    bias = synth.normal(75, 0, 48, 1.0)
+    tb = torch.from_numpy(bias).to(dev)
+    a = torch.zeros((0, 32), dtype=torch.uint8, device=dev)          # [K=0, M=32] MN-major
+    b = torch.zeros((0, 48), dtype=torch.uint8, device=dev)          # [K=0, N=48] MN-major
+    out, amax = q.qgemm(a, "e4m3", b, "e4m3", s1, s1, a_layout="mn_major", b_layout="mn_major", bias=tb,
+                        out_dtype="fp32", out_amax=True, K=0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), tb.cpu().expand(32, 48)) and amax.item() == np.abs(bias).max()
+    # M = 0 through the C ABI: A's storage is [K=64, lda=16] with no columns used.
+    M, N, K = 0, 32, 64
+    a_st = torch.zeros((K, 16), dtype=torch.uint8, device=dev)
+    b_st = torch.zeros((K, N), dtype=torch.uint8, device=dev)
+    o = torch.full((4,), 7.0, device=dev)
+    am = torch.full((1,), 5.0, device=dev)
+    ws = q.workspace()
+    q.ql_qgemm(a_st.data_ptr(), 0, _lib.QL_MN_MAJOR, 16, b_st.data_ptr(), 0, _lib.QL_MN_MAJOR, N, M, N, K,
+               s1.data_ptr(), 0, s1.data_ptr(), 0, None, 0, o.data_ptr(), _lib.QL_DT_FP32, N, None, am.data_ptr(),
+               ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (o.cpu() == 7.0).all() and am.item() == 0.0
+    # N = 0
+    a_st = torch.zeros((K, 32), dtype=torch.uint8, device=dev)
+    out, amax = q.qgemm(a_st, "e4m3", torch.zeros((K, 0), dtype=torch.uint8, device=dev), "e4m3", s1, s1,
+                        a_layout="mn_major", b_layout="mn_major", out_dtype="bf16", out_amax=True, K=K)
+    torch.cuda.synchronize()
+    assert out.shape == (32, 0) and amax.item() == 0.0
