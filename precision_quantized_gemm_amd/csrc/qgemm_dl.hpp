@@ -15,13 +15,9 @@
 //     128 k-bytes, chunk swizzle lds_swz) and read with ds_read_b128.
 //   * An MN-major operand is stored as it lies in memory, one row per k
 //     (R mn-bytes, R = tile rows), with its 16-byte chunks XOR-swizzled by a
-//     function of k, and read with ds_read_b64_tr_b8.  That instruction
-//     serves blocks of 16 lanes: byte j returned to lane i is byte (i & 7)
-//     of the 8 bytes addressed by lane 2j + (i >= 8) of the block (measured
-//     with an in-bounds probe over three address patterns).  So lanes 2j and
-//     2j+1 of a block point at k-row k0 + j, mn bytes [m, m+8) and
-//     [m+8, m+16), and lane i receives k0 .. k0+7 of mn row m + i: the
-//     16x16x128 operand layout, 8 k at a time (4 reads per fragment).
+//     function of k (mn_swz), and read with ds_read_b64_tr_b8 as
+//     load_frag_tr in qgemm_impl.hpp describes: 8 k at a time, 4 reads per
+//     16x16x128 fragment.
 //   * Matrix cores, tile shape, epilogue and tile order as the general kernel
 //     (v_mfma_f32_16x16x128_f8f6f4, or paired i8 16x16x64).
 // Requirements (checked on the host, p.fast): 16-byte aligned operands and
@@ -37,19 +33,7 @@
 
 namespace ql {
 
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *dl_lds_ptr_t;
-typedef __attribute__((address_space(3))) v2i *dl_lds_v2i_t;
-
-// Chunk swizzle of an MN-major k-row of R bytes: spreads the 8 k-rows of a
-// transpose read (and the two blocks of 16 lanes served with them) over all
-// banks.  Brute-force checked conflict-free for 16- and 32-lane groups.
-template <int R> __device__ __forceinline__ int dl_mn_swz(int kr)
-{
-    static_assert(R == 128 || R == 64, "MN-major tile rows");
-    if constexpr (R == 128) return ((kr >> 1) & 3) | (((kr >> 5) & 1) << 2);
-    else return ((kr >> 2) & 1) | (((kr >> 5) & 1) << 1);
-}
 
 // One operand of one k-step: R rows (tile rows) x 128 k.  R/32 direct loads
 // per wave; load j of wave w fills bytes [(4j + w) * 1024, +1024) of the
@@ -88,7 +72,7 @@ template <int R, bool MN> struct DlOperand {
                 off[j] = (uint32_t)(row * ld + c * 16);
             } else {
                 const int kr = L / R, pos = (L % R) >> 4;
-                const int c = pos ^ dl_mn_swz<R>(kr);
+                const int c = pos ^ mn_swz<R>(kr);
                 kc[j] = 0;
                 off[j] = (uint32_t)(kr * ld + c * 16);
             }
@@ -203,7 +187,7 @@ __device__ __forceinline__ void dl_frag_offsets(int row0, int lane, uint32_t (&o
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int kr = 32 * b + 8 * q + (t >> 1);
-            off[q] = (uint32_t)(kr * R + ((c ^ dl_mn_swz<R>(kr)) << 4) + 8 * h);
+            off[q] = (uint32_t)(kr * R + ((c ^ mn_swz<R>(kr)) << 4) + 8 * h);
         }
     }
 }

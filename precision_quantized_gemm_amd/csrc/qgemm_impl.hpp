@@ -14,8 +14,10 @@
 //     loads of step k+2 are in flight while the matrix cores work on step k.
 //   * LDS holds every operand K-major (128 bytes per row) with a 16-byte
 //     chunk swizzle, so the fragment reads (one row per lane, two 16-byte
-//     chunks) are free of bank conflicts.  MN-major operands are transposed
-//     in registers (byte shuffles) on their way into LDS.
+//     chunks) are free of bank conflicts.  MN-major operands reach this
+//     kernel only when unaligned or ragged (aligned ones take the
+//     direct-to-LDS kernel); they are bounds-checked and transposed in
+//     registers (byte permutes) on their way into LDS.
 //   * FP8: v_mfma_f32_16x16x128_f8f6f4 with per-operand formats (E4M3 and
 //     E5M2 mix freely).  INT8: two v_mfma_i32_16x16x64_i8 per 128 bytes,
 //     exact in INT32.  Each lane's 32 fragment bytes are 32 consecutive k, so
@@ -39,6 +41,20 @@ namespace ql {
 constexpr int GEMM_BK = 128;
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 7); }
 __device__ __forceinline__ int lds_off(int r, int chunk) { return r * GEMM_BK + ((chunk ^ lds_swz(r)) << 4); }
+
+// MN-major operand in LDS (direct-to-LDS kernel): stored as it lies in
+// memory, one row of R mn-bytes per k, with its 16-byte chunks XOR-swizzled
+// by a function of k so that its transpose reads (8 k-rows at one mn offset
+// per 16-lane block, two blocks served together) hit distinct banks;
+// brute-force checked for 16- and 32-lane groups.
+template <int R> __device__ __forceinline__ int mn_swz(int kr)
+{
+    static_assert(R == 256 || R == 128 || R == 64, "MN-major tile rows");
+    if constexpr (R == 256) return (kr & 7) | (((kr >> 5) & 1) << 3);
+    else if constexpr (R == 128) return ((kr >> 1) & 3) | (((kr >> 5) & 1) << 2);
+    else return ((kr >> 2) & 1) | (((kr >> 5) & 1) << 1);
+}
+__device__ __forceinline__ int mn_off(int R, int kr, int chunk, int swz) { return kr * R + ((chunk ^ swz) << 4); }
 
 // Load up to 16 bytes [p, p + n) into a zero-padded 16-byte vector.
 __device__ __forceinline__ uint4 load_partial(const uint8_t *p, int64_t n)
@@ -221,57 +237,6 @@ template <int ROWS> struct FastStage<ROWS, false> {
         for (int i = 0; i < PER; ++i) {
             const int c = i * GEMM_THREADS + (int)threadIdx.x;
             *reinterpret_cast<uint4 *>(lds + lds_off(c >> 3, c & 7)) = r[i];
-        }
-    }
-};
-
-template <int ROWS> struct FastStage<ROWS, true> {
-    static constexpr int GROUPS = ROWS / 16;
-    static constexpr int UNITS = GROUPS * (GEMM_BK / 8);
-    static_assert(UNITS % GEMM_THREADS == 0 || UNITS < GEMM_THREADS, "unit split");
-    static constexpr int PER = (UNITS + GEMM_THREADS - 1) / GEMM_THREADS;
-    uint4 r[PER][8];
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t off[PER];      // (kq*8) * ld + mn, tile relative; OOB when mn is past the matrix
-    uint32_t ld32;
-    __device__ __forceinline__ void init(const uint8_t *base, int64_t ld, int64_t row0, int64_t rows_total, int64_t K)
-    {
-        const int64_t bytes = K * ld - row0;          // rows k >= K fall outside
-        rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(base + row0), (short)0,
-                                                 (int)(bytes > 0 ? (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0), BUF_WORD3);
-        ld32 = (uint32_t)ld;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int u = i * GEMM_THREADS + (int)threadIdx.x;
-            const int mg = u % GROUPS, kq = u / GROUPS;
-            const bool ok = u < UNITS && row0 + mg * 16 < rows_total;
-            off[i] = ok ? (uint32_t)(kq * 8 * ld + mg * 16) : BUF_OOB;
-        }
-    }
-    __device__ __forceinline__ void load(int64_t k0, int64_t K)
-    {
-        (void)K;
-        const uint32_t kb = (uint32_t)k0 * ld32;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r[i][j] = buf_load16(rsrc, off[i] == BUF_OOB ? BUF_OOB : off[i] + kb + (uint32_t)j * ld32);
-    }
-    __device__ __forceinline__ void store(uint8_t *lds) const
-    {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int u = i * GEMM_THREADS + (int)threadIdx.x;
-            if (u >= UNITS) continue;
-            const int mg = u % GROUPS, kq = u / GROUPS;
-            uint32_t lo[16], hi[16];
-            transpose_8x16_bytes(r[i], lo, hi);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = mg * 16 + e;
-                *reinterpret_cast<uint2 *>(lds + lds_off(row, kq >> 1) + (kq & 1) * 8) = make_uint2(lo[e], hi[e]);
-            }
         }
     }
 };
@@ -498,14 +463,8 @@ hipError_t launch_dl(GemmParams p, hipStream_t s);
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)
 {
-    const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    // K-major operands with at least one 256 x 256 tile per CU: the
-    // pipelined direct-to-LDS kernel.
-    // The pipelined kernel covers FP8 only: INT8's paired 32-deep MFMAs do
-    // not fit its register budget.
-    if constexpr (AF != FMT_INT8)
-        if (p.fast && !A_MN && !B_MN && big >= 256 && p.batch <= 1) return launch_nt<AF, BF>(p, s);
-    if (p.fast && (A_MN || B_MN)) {
+    if constexpr (A_MN || B_MN) {
+        if (!p.fast) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false, 1>(p, s);
         // An MN-major operand: the direct-to-LDS kernel (transpose reads).
         // Tiles and ring depth keep two workgroups per CU where the grid
         // allows it (measured on the 2048 x 4096 x 1024 backward products):
@@ -518,19 +477,28 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         if (t128 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 128, 4, 1>(p, s);
         if (t128x64 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 64, 3, 1>(p, s);
         return launch_dl<AF, BF, A_MN, B_MN, 64, 64, 4, 2>(p, s);
+    } else {
+        // Both operands K-major.
+        const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        // K-major operands with at least one 256 x 256 tile per CU: the
+        // pipelined direct-to-LDS kernel.
+        // The pipelined kernel covers FP8 only: INT8's paired 32-deep MFMAs do
+        // not fit its register budget.
+        if constexpr (AF != FMT_INT8)
+            if (p.fast && big >= 256 && p.batch <= 1) return launch_nt<AF, BF>(p, s);
+        if (p.fast) {
+            // The largest tile that still gives every CU a workgroup (batch
+            // items count: they are grid rows).
+            const int64_t nb = p.batch > 1 ? p.batch : 1;
+            const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
+            const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
+            if (big * nb >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true, 1>(p, s);
+            if (t128 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 1, true, 2>(p, s);
+            if (t128x64 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 64, 2, true, 2>(p, s);
+            return launch_tile<AF, BF, A_MN, B_MN, 64, 64, 2, true, 2>(p, s);
+        }
+        return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false, 1>(p, s);
     }
-    if (p.fast) {
-        // The largest tile that still gives every CU a workgroup (batch
-        // items count: they are grid rows).
-        const int64_t nb = p.batch > 1 ? p.batch : 1;
-        const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
-        const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
-        if (big * nb >= 512) return launch_tile<AF, BF, A_MN, B_MN, 256, 256, 1, true, 1>(p, s);
-        if (t128 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 1, true, 2>(p, s);
-        if (t128x64 >= 256) return launch_tile<AF, BF, A_MN, B_MN, 128, 64, 2, true, 2>(p, s);
-        return launch_tile<AF, BF, A_MN, B_MN, 64, 64, 2, true, 2>(p, s);
-    }
-    return launch_tile<AF, BF, A_MN, B_MN, 128, 128, 2, false, 1>(p, s);
 }
 
 template <int AF, int BF>
