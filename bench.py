@@ -229,6 +229,96 @@ def sclk_under(fn, torch, launches):
     return round(sum(core) / len(core), 1) if core else None
 
 
+def time_configs(torch, q, _lib, synth, dev, reps):
+    """The small configurations of the method on the same library calls:
+    the tiny linear layer (linear_forward, x [512,128], W [128,128]), per-row
+    INT8 (quantize a [128,1024] and b [512,1024] per row, INT8 GEMM, FP32
+    out = acc * sa[m] * sb[n]) and the MLP-up layer (linear_forward, x
+    [2048,1024], W [4096,1024]).  Each step is timed eagerly and as a
+    replayed HIP graph of the same calls (no host launch cost); the graph's
+    result is checked against the eager one."""
+    P = lambda t: None if t is None else t.data_ptr()
+    f1 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
+    ws = q.new_workspace(dev)
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    out = {}
+
+    def linear(name, x, w, bias):
+        M, K = x.shape
+        N = w.shape[0]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sx, ax, sw, aw = f1(), f1(), f1(), f1()
+        run = lambda: q.ql_linear_forward(P(x), _lib.QL_DT_BF16, M, K, P(w), N, P(bias), _lib.QL_DT_FP32,
+                                          _lib.QL_FMT_E4M3, None, None, P(y), _lib.QL_DT_BF16, None, None,
+                                          P(xq), P(sx), P(ax), P(wq), P(sw), P(aw), P(ws), stream())
+        return run, y, 2.0 * M * N * K
+
+    def rowwise(a, b):
+        M, K = a.shape
+        N = b.shape[0]
+        aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        bq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sa, am = torch.empty(M, device=dev), torch.empty(M, device=dev)
+        sb, bm = torch.empty(N, device=dev), torch.empty(N, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def run():
+            q.ql_quantize(P(a), _lib.QL_DT_FP32, M, K, K, _lib.QL_PER_ROW, _lib.QL_FMT_INT8, None, P(aq), K, P(sa),
+                          P(am), None, stream())
+            q.ql_quantize(P(b), _lib.QL_DT_FP32, N, K, K, _lib.QL_PER_ROW, _lib.QL_FMT_INT8, None, P(bq), K, P(sb),
+                          P(bm), None, stream())
+            q.ql_qgemm(P(aq), _lib.QL_FMT_INT8, _lib.QL_K_MAJOR, K, P(bq), _lib.QL_FMT_INT8, _lib.QL_K_MAJOR, K,
+                       M, N, K, P(sa), _lib.QL_PER_ROW, P(sb), _lib.QL_PER_ROW, None, 0, P(y), _lib.QL_DT_FP32, N,
+                       None, None, P(ws), stream())
+        return run, y, 2.0 * M * N * K
+
+    t1 = synth.workload("tiny_linear")
+    t2 = synth.workload("rowwise_int8")
+    t3 = synth.workload("mlp_up")
+    cases = {
+        "tiny_linear": linear("tiny_linear", t1["x"].to(dev), t1["w"].to(dev), t1["bias"].to(dev)),
+        "rowwise_int8": rowwise(t2["a"].to(dev), t2["b"].to(dev)),
+        "mlp_up": linear("mlp_up", t3["x"].to(dev), t3["w"].to(dev), t3["bias"].to(dev)),
+    }
+    for name, (run, y, flops) in cases.items():
+        for _ in range(3):
+            run()
+        ms_eager = time_events(run, reps, torch)
+        torch.cuda.synchronize()
+        ref = y.clone()
+        entry = {"ms_eager": round(ms_eager, 5), "TFLOPs_eager": round(flops / (ms_eager * 1e-3) / 1e12, 2)}
+        out[name] = entry
+        try:
+            entry.update(graph_replay(run, y, ref, flops, torch, reps))
+        except RuntimeError as e:                  # report, keep the benchmark line
+            entry["graph_error"] = str(e)[:200]
+    return out
+
+
+def graph_replay(run, y, ref, flops, torch, reps):
+    """Capture run() once in a HIP graph, replay it `reps` times; the result
+    must equal the eager one after every timing."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y, ref))
+    ms_graph = time_events(g.replay, reps, torch)
+    torch.cuda.synchronize()
+    same = same and bool(torch.equal(y, ref))
+    return {"ms_graph_replay": round(ms_graph, 5), "TFLOPs_graph": round(flops / (ms_graph * 1e-3) / 1e12, 2),
+            "graph_matches_eager": same}
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -405,6 +495,9 @@ def main():
     log("per-head batched products")
     per_head = time_per_head(torch, q, _lib, synth, dev, args.steps)
 
+    log("small configurations")
+    small = time_configs(torch, q, _lib, synth, dev, args.steps)
+
     log("shader clock under the GEMM")
     sclk = sclk_under(gemm, torch, 500)
 
@@ -464,6 +557,7 @@ def main():
                              "workload": "ql_linear_forward_static: quantize a, GEMM with the pre-quantized b"},
         "linear_backward": bwd,
         "per_head": per_head,
+        "small_configs": small,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
         "wall_s_timed_region": round(t_wall, 4),
