@@ -273,3 +273,32 @@ def test_groups_on_pipelined_path(orc):
     got = _vals(out.cpu())[0][ms, ns]
     print("groups on pipelined", check_float(got, v, S, H, _scales_sasb(sa, ga, sb, gb, zs, ms, ns, M, N), K,
                                              what="groups pipelined"))
+
+
+@pytest.mark.parametrize("al,bl", [(1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("pad", [0, 8])
+def test_batched_mn_major(orc, al, bl, pad):
+    """Batched products with MN-major operands: item strides that keep every
+    item 16-byte aligned take the direct-to-LDS kernel, strides padded by 8
+    bytes the bounds-checked general kernel; per-item scales on both sides."""
+    batch, M, N, K = 3, 48, 80, 96
+    a_log = _codes(orc, 101, al, (batch, M, K), 0)
+    b_log = _codes(orc, 102, bl, (batch, N, K), 1)
+
+    def pack(log, lay, rows):
+        items = [np.ascontiguousarray(log[z] if lay == 0 else log[z].T) for z in range(batch)]
+        st = items[0].size + pad
+        buf = np.zeros(batch * st, np.uint8)
+        for z in range(batch):
+            buf[z * st: z * st + items[z].size] = items[z].ravel()
+        return buf, st, (K if lay == 0 else rows)
+
+    a_st, sta, lda = pack(a_log, al, M)
+    b_st, stb, ldb = pack(b_log, bl, N)
+    sa = np.array([0.01, 0.02, 0.005], np.float32)
+    sb = np.array([0.03, 0.004, 0.01], np.float32)
+    out, _ = _batched_raw(a_st, 0, al, lda, sta, b_st, 1, bl, ldb, stb, batch, M, N, K, sa, M, sb, N, out_dt="fp32")
+    zs, ms, ns = _all_zmn(batch, M, N)
+    acc, S, H, v = orc.qgemm_batched_entries(a_log, 0, b_log, 1, zs, ms, ns, sa, M, sb, N)
+    got = out.numpy().reshape(batch, M, N)[zs, ms, ns].astype(np.float64)
+    check_float(got, v, S, H, _scales_sasb(sa, M, sb, N, zs, ms, ns, M, N), K, what=f"batched mn {al},{bl} pad={pad}")
