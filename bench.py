@@ -319,6 +319,29 @@ def graph_replay(run, y, ref, flops, torch, reps):
             "graph_matches_eager": same}
 
 
+def time_int8_large(torch, q, _lib, dev, M, N, K, reps):
+    """INT8 GEMM at the benchmark shape (an extra, clearly INT8: random codes
+    in [-127, 127], per-row scales, raw INT32 accumulator output), on the
+    general kernel."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0x5EED0008)
+    a = torch.randint(-127, 128, (M, K), device=dev, dtype=torch.int32, generator=g).to(torch.int8)
+    b = torch.randint(-127, 128, (N, K), device=dev, dtype=torch.int32, generator=g).to(torch.int8)
+    s1 = torch.ones(max(M, N), device=dev)
+    out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    run = lambda: q.ql_qgemm(a.data_ptr(), _lib.QL_FMT_INT8, _lib.QL_K_MAJOR, K, b.data_ptr(), _lib.QL_FMT_INT8,
+                             _lib.QL_K_MAJOR, K, M, N, K, s1.data_ptr(), _lib.QL_PER_ROW, s1.data_ptr(),
+                             _lib.QL_PER_ROW, None, 0, out.data_ptr(), _lib.QL_DT_INT32, N, None, None, None, stream)
+    for _ in range(2):
+        run()
+    ms = time_events(run, reps, torch)
+    ops = 2.0 * M * N * K
+    del a, b, out
+    return {"workload": f"INT8 {M}x{N}x{K}, per-row scales, INT32 out", "ms_per_launch": round(ms, 5),
+            "TOPs": round(ops / (ms * 1e-3) / 1e12, 1), "frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / 5000.0, 4)}
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -498,6 +521,9 @@ def main():
     log("small configurations")
     small = time_configs(torch, q, _lib, synth, dev, args.steps)
 
+    log("INT8 at the benchmark shape")
+    int8 = time_int8_large(torch, q, _lib, dev, M, N, K, 10)
+
     log("shader clock under the GEMM")
     sclk = sclk_under(gemm, torch, 500)
 
@@ -558,6 +584,7 @@ def main():
         "linear_backward": bwd,
         "per_head": per_head,
         "small_configs": small,
+        "int8_large": int8,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
         "wall_s_timed_region": round(t_wall, 4),
