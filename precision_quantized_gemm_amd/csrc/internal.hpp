@@ -56,7 +56,17 @@ struct QzParams {
     float *scale_used;
 };
 
+// Up to two whole-tensor quantizes in one launch per pass (grid row y
+// works on tensor y, each with its own workspace slot and election).
+struct QzPack {
+    QzParams t[2];
+};
+
 hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s);
+// Quantize two tensors of the same input dtype and format: one launch per
+// pass when both are whole-tensor quantizes of the same kind, else one
+// after the other.
+hipError_t launch_quantize_pair(const QzParams &p0, const QzParams &p1, int in_dt, int fmt, hipStream_t s);
 // grad_bias: out[n] = sum_m g[m, n] for BF16 g [M, N] (leading dimension ldg);
 // partials: WS_PART_BYTES of scratch (the workspace's partial area).
 hipError_t launch_col_sum_bf16(const void *g, int64_t M, int64_t N, int64_t ldg, float *out, float *partials,

@@ -193,16 +193,24 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 // system (about 10 ns each on MI355X), and the acquire-release increment
 // also writes back and invalidates the XCD's L2.  Grids that finish all at
 // once (the streaming quantize kernels) therefore stay at a few hundred
-// workgroups; the grid must be one-dimensional.
-__device__ __forceinline__ bool elect_last_max(uint32_t *slot, uint32_t block_max, uint32_t *result)
+// workgroups.  `count` is the number of workgroups that take part (a grid
+// row, when the rows of a grid are independent elections).
+__device__ __forceinline__ bool elect_last_max_n(uint32_t *slot, uint32_t block_max, uint32_t *result,
+                                                 uint32_t count)
 {
     __hip_atomic_fetch_max(&slot[0], block_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t prev = __hip_atomic_fetch_add(&slot[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev != gridDim.x * gridDim.y - 1) return false;
+    if (prev != count - 1) return false;
     *result = __hip_atomic_load(&slot[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&slot[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&slot[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     return true;
+}
+
+// The election over the whole grid.
+__device__ __forceinline__ bool elect_last_max(uint32_t *slot, uint32_t block_max, uint32_t *result)
+{
+    return elect_last_max_n(slot, block_max, result, gridDim.x * gridDim.y);
 }
 
 }  // namespace ql

@@ -329,10 +329,9 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                               ql::ws_slot(ws, ql::WS_SLOT_QA));
     ql::QzParams pw = make_qz(w, x_dt, N, K, K, QL_PER_TENSOR, fmt, sw_in, w_q, K, sw, amax_w,
                               ql::ws_slot(ws, ql::WS_SLOT_QB));
-    hipError_t e = ql::launch_quantize(px, x_dt, fmt, s);
-    if (e != hipSuccess) return hip_status(e, "linear_forward: quantize x");
-    e = ql::launch_quantize(pw, x_dt, fmt, s);
-    if (e != hipSuccess) return hip_status(e, "linear_forward: quantize w");
+    // x and w share each pass's launch (one grid row each).
+    const hipError_t e = ql::launch_quantize_pair(px, pw, x_dt, fmt, s);
+    if (e != hipSuccess) return hip_status(e, "linear_forward: quantize x and w");
     ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
     return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
 }

@@ -152,8 +152,9 @@ __device__ __forceinline__ void ring_publish(const QzParams &p, uint32_t bits, u
 // ---------------------------------------------------------------------------
 // Pass 1 of per-tensor current scaling.
 template <typename T, int MODE>
-__global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzParams p)
+__global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzPack pk)
 {
+    const QzParams &p = pk.t[blockIdx.y];
     const T *x = static_cast<const T *>(p.x);
     const int64_t gtid = (int64_t)blockIdx.x * QZ_THREADS + threadIdx.x;
     const int64_t gstride = (int64_t)gridDim.x * QZ_THREADS;
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzParams p)
     m = block_max_u32(m, red);
     if (threadIdx.x == 0) {
         uint32_t bits;
-        if (elect_last_max(p.ws, m, &bits)) publish(p, bits, 0);
+        if (elect_last_max_n(p.ws, m, &bits, gridDim.x)) publish(p, bits, 0);
     }
 }
 
@@ -204,8 +205,9 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzParams p)
 // Cast with one step for the whole tensor.  MEASURE (delayed scaling): the
 // step comes from the caller and amax is measured in the same pass.
 template <typename T, int FMT, int MODE, bool MEASURE>
-__global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
+__global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzPack pk)
 {
+    const QzParams &p = pk.t[blockIdx.y];
     const T *x = static_cast<const T *>(p.x);
     uint8_t *xq = static_cast<uint8_t *>(p.xq);
     const Divider div(p.scale_src[0]);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzParams p)
         m = block_max_u32(m, red);
         if (threadIdx.x == 0) {
             uint32_t bits = 0;
-            const bool last = elect_last_max(p.ws, m, &bits);
+            const bool last = elect_last_max_n(p.ws, m, &bits, gridDim.x);
             if (last && !p.ring) publish(p, bits, 0);
             is_last = last;
             last_bits = bits;
@@ -389,18 +391,32 @@ static int blocks_for(int64_t work)
     return (int)b;
 }
 
+static int64_t tensor_work(const QzParams &p, int mode)
+{
+    return mode == MODE_SCALAR ? p.n_elems : (p.n_units > 0 ? p.n_units : p.n_elems);
+}
+
+// ntensors (1 or 2) whole-tensor quantizes of the same mode and kind
+// (current or delayed scaling), grid row y on tensor y.
+template <typename T, int FMT, int MODE>
+static hipError_t launch_tensor_pack(const QzPack &pk, int ntensors, hipStream_t s)
+{
+    int64_t work = tensor_work(pk.t[0], MODE);
+    if (ntensors > 1 && tensor_work(pk.t[1], MODE) > work) work = tensor_work(pk.t[1], MODE);
+    const dim3 grid(blocks_for(work), ntensors);
+    if (pk.t[0].delayed) {
+        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), grid, dim3(QZ_THREADS), 0, s, pk);
+    } else {
+        hipLaunchKernelGGL((qz_amax<T, MODE>), grid, dim3(QZ_THREADS), 0, s, pk);
+        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, false>), grid, dim3(QZ_THREADS), 0, s, pk);
+    }
+    return hipGetLastError();
+}
+
 template <typename T, int FMT, int MODE>
 static hipError_t launch_tensor_mode(const QzParams &p, hipStream_t s)
 {
-    const int64_t work = MODE == MODE_SCALAR ? p.n_elems : (p.n_units > 0 ? p.n_units : p.n_elems);
-    const int blocks = blocks_for(work);
-    if (p.delayed) {
-        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
-    } else {
-        hipLaunchKernelGGL((qz_amax<T, MODE>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
-        hipLaunchKernelGGL((qz_cast<T, FMT, MODE, false>), dim3(blocks), dim3(QZ_THREADS), 0, s, p);
-    }
-    return hipGetLastError();
+    return launch_tensor_pack<T, FMT, MODE>(QzPack{{p, p}}, 1, s);
 }
 
 template <typename T, int FMT>
@@ -423,6 +439,35 @@ static hipError_t launch_fmt(const QzParams &p, hipStream_t s)
     case MODE_ROWS: return launch_tensor_mode<T, FMT, MODE_ROWS>(p, s);
     default: return launch_tensor_mode<T, FMT, MODE_SCALAR>(p, s);
     }
+}
+
+template <typename T, int FMT>
+static hipError_t launch_pair_fmt(const QzParams &p0, const QzParams &p1, hipStream_t s)
+{
+    const bool pack = !p0.per_row && !p1.per_row && p0.mode == p1.mode && p0.delayed == p1.delayed && !p0.ring &&
+                      !p1.ring;
+    if (!pack) {
+        const hipError_t e = launch_fmt<T, FMT>(p0, s);
+        return e != hipSuccess ? e : launch_fmt<T, FMT>(p1, s);
+    }
+    const QzPack pk{{p0, p1}};
+    switch (p0.mode) {
+    case MODE_FLAT: return launch_tensor_pack<T, FMT, MODE_FLAT>(pk, 2, s);
+    case MODE_ROWS: return launch_tensor_pack<T, FMT, MODE_ROWS>(pk, 2, s);
+    default: return launch_tensor_pack<T, FMT, MODE_SCALAR>(pk, 2, s);
+    }
+}
+
+hipError_t launch_quantize_pair(const QzParams &p0, const QzParams &p1, int in_dt, int fmt, hipStream_t s)
+{
+    if (in_dt == DT_BF16) {
+        if (fmt == FMT_E4M3) return launch_pair_fmt<uint16_t, FMT_E4M3>(p0, p1, s);
+        if (fmt == FMT_E5M2) return launch_pair_fmt<uint16_t, FMT_E5M2>(p0, p1, s);
+        return launch_pair_fmt<uint16_t, FMT_INT8>(p0, p1, s);
+    }
+    if (fmt == FMT_E4M3) return launch_pair_fmt<float, FMT_E4M3>(p0, p1, s);
+    if (fmt == FMT_E5M2) return launch_pair_fmt<float, FMT_E5M2>(p0, p1, s);
+    return launch_pair_fmt<float, FMT_INT8>(p0, p1, s);
 }
 
 hipError_t launch_quantize(const QzParams &p, int in_dt, int fmt, hipStream_t s)
