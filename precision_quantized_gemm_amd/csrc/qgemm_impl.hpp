@@ -54,7 +54,6 @@ template <int R> __device__ __forceinline__ int mn_swz(int kr)
     else if constexpr (R == 128) return ((kr >> 1) & 3) | (((kr >> 5) & 1) << 2);
     else return ((kr >> 2) & 1) | (((kr >> 5) & 1) << 1);
 }
-__device__ __forceinline__ int mn_off(int R, int kr, int chunk, int swz) { return kr * R + ((chunk ^ swz) << 4); }
 
 // Load up to 16 bytes [p, p + n) into a zero-padded 16-byte vector.
 __device__ __forceinline__ uint4 load_partial(const uint8_t *p, int64_t n)
