@@ -83,12 +83,15 @@ typedef enum { QL_K_MAJOR = 0, QL_MN_MAJOR = 1 } ql_layout;
  * leaves them reset to zero, so a workspace is zeroed once, at allocation,
  * and never again (the zero-fill dispatch per quantize that [FP8PY]'s commit
  * message removes is not needed at all).  Behind those words the workspace
- * holds 1 MiB of scratch for grad_bias's partial column sums, which every
- * use overwrites.  Calls that share a workspace must be ordered (same stream
- * or explicit events); concurrent calls need separate workspaces.
+ * holds scratch that every use overwrites: 1 MiB for grad_bias's partial
+ * column sums and 256 KiB for the per-workgroup maxima of a GEMM's
+ * out_amax (reduced by a one-workgroup kernel after the GEMM, which keeps
+ * the GEMM's workgroups free of device-scope synchronization).  Calls that
+ * share a workspace must be ordered (same stream or explicit events);
+ * concurrent calls need separate workspaces.
  * ---------------------------------------------------------------------- */
 
-/* Size in bytes of one workspace (a constant, 1 KiB + 1 MiB). */
+/* Size in bytes of one workspace (a constant, 1 KiB + 1.25 MiB). */
 size_t ql_workspace_bytes(void);
 
 /* Zero a freshly allocated workspace of `bytes` bytes on `stream` (a fill

@@ -19,9 +19,15 @@ constexpr int64_t WS_SLOT_GEMM = 2;    // GEMM output amax
 constexpr int64_t WS_COUNTER_BYTES = 4 * WS_SLOT_BYTES;   // zeroed once, left zeroed by every call
 // Partial column sums of grad_bias (no zeroing needed: fully overwritten).
 constexpr int64_t WS_PART_BYTES = (int64_t)1 << 20;
-constexpr int64_t WS_BYTES = WS_COUNTER_BYTES + WS_PART_BYTES;
+// Per-workgroup maxima of a GEMM's out_amax (fully overwritten per call).
+constexpr int64_t WS_AMAX_PARTS = (int64_t)1 << 16;
+constexpr int64_t WS_BYTES = WS_COUNTER_BYTES + WS_PART_BYTES + WS_AMAX_PARTS * 4;
 
 inline float *ws_partials(void *ws) { return reinterpret_cast<float *>(static_cast<char *>(ws) + WS_COUNTER_BYTES); }
+inline uint32_t *ws_amax_parts(void *ws)
+{
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + WS_COUNTER_BYTES + WS_PART_BYTES);
+}
 
 inline uint32_t *ws_slot(void *ws, int64_t slot)
 {
@@ -118,7 +124,11 @@ struct GemmParams {
     int out_dt;                     // DT_BF16 / DT_FP32 / DT_E4M3 / DT_INT32
     const float *out_scale;
     float *out_amax;
-    uint32_t *ws;                   // workspace slot for out_amax
+    uint32_t *ws;                   // workspace slot for the out_amax election
+    // out_amax without an election: workgroup w stores its maximum at
+    // amax_part[w] and a one-workgroup kernel reduces them after the GEMM
+    // (null: the election, for grids larger than the array).
+    uint32_t *amax_part;
     int a_aligned, b_aligned;       // 16-byte loads allowed
     int out_vec4;                   // 4 consecutive outputs may be stored as one vector
     int out_vec16;                  // 16 consecutive outputs (16-aligned column) are 16-byte vectors
@@ -134,6 +144,10 @@ inline void finish_groups(GemmParams &p)
     p.sa_div.init(p.sa_group);
     p.sb_div.init(p.sb_group);
 }
+
+// out_amax of a GEMM whose nblocks workgroups stored their maxima at
+// p.amax_part (run right after the GEMM on the same stream).
+hipError_t launch_amax_finalize(const GemmParams &p, int64_t nblocks, hipStream_t s);
 
 // a_fmt / b_fmt: FMT_*; a_mn / b_mn: operand stored MN-major.
 hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s);

@@ -116,6 +116,25 @@ struct Epilogue {
     }
 };
 
+// End of a GEMM workgroup's out_amax: the workgroup maximum goes to its
+// own slot of p.amax_part (reduced by a small kernel after the GEMM), or,
+// without that array, into the last-workgroup election.  The election's
+// device-scope acquire-release increment writes back and invalidates the
+// XCD's L2, which in a grid of short-lived tiles throws away the operand
+// panels the other tiles of that XCD are reusing.
+__device__ __forceinline__ void gemm_publish_amax(const GemmParams &p, uint32_t vmax, uint32_t *red)
+{
+    vmax = block_max_u32(vmax, red);
+    if (threadIdx.x == 0) {
+        if (p.amax_part) {
+            p.amax_part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = vmax;
+        } else {
+            uint32_t bits;
+            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
+        }
+    }
+}
+
 // Linear workgroup id -> (tile_m, tile_n): XCD-contiguous, then grouped.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn)
 {

@@ -294,12 +294,15 @@ hipError_t launch_dl(GemmParams p, hipStream_t s)
 {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);
-    if (p.tiles_m == 0 || p.tiles_n == 0) p.tiles_m = p.tiles_n = 1;   // as launch_tile: publishes out_amax = 0
+    if (p.tiles_m == 0 || p.tiles_n == 0) p.tiles_m = p.tiles_n = 1;   // as launch_tile: out_amax = 0
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
+    if (grid * batch > WS_AMAX_PARTS) p.amax_part = nullptr;
     hipLaunchKernelGGL((qgemm_dl_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, MINW>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.out_amax || !p.amax_part) return e;
+    return launch_amax_finalize(p, grid * batch, s);
 }
 
 }  // namespace ql

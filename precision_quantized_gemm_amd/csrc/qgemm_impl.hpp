@@ -336,13 +336,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmParams &p, uint8_t *lds,
             if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w, row, col, vmax);
         }
     }
-    if (p.out_amax) {
-        vmax = block_max_u32(vmax, red);
-        if (threadIdx.x == 0) {
-            uint32_t bits;
-            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
-        }
-    }
+    if (p.out_amax) gemm_publish_amax(p, vmax, red);
 }
 
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int MINW, bool FAST, int PF>
@@ -441,14 +435,17 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
     if (p.tiles_m == 0 || p.tiles_n == 0) {
         // Empty output: one workgroup whose tile lies wholly outside it
         // (every load reads zeros, no store happens); it still publishes
-        // out_amax = 0 through the election.
+        // out_amax = 0.
         p.tiles_m = p.tiles_n = 1;
     }
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
+    if (grid * batch > WS_AMAX_PARTS) p.amax_part = nullptr;
     hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST, PF>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.out_amax || !p.amax_part) return e;
+    return launch_amax_finalize(p, grid * batch, s);
 }
 
 // Tile size (general kernel): 256 x 256 when that still gives at least two

@@ -442,13 +442,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
             }
         }
     }
-    if (p.out_amax) {
-        vmax = block_max_u32(vmax, red);
-        if (threadIdx.x == 0) {
-            uint32_t bits;
-            if (elect_last_max(p.ws, vmax, &bits)) p.out_amax[0] = __uint_as_float(bits);
-        }
-    }
+    if (p.out_amax) gemm_publish_amax(p, vmax, red);
 }
 
 template <int AF, int BF>
@@ -457,11 +451,14 @@ hipError_t launch_nt(GemmParams p, hipStream_t s)
     p.tiles_m = (int)((p.M + NT_BM - 1) / NT_BM);
     p.tiles_n = (int)((p.N + NT_BN - 1) / NT_BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
     if (p.K % NT_BK == 0)
         hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
     else
         hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, true>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.out_amax || !p.amax_part) return e;
+    return launch_amax_finalize(p, grid, s);
 }
 
 }  // namespace ql

@@ -208,6 +208,7 @@ ql::GemmParams make_gemm(const GemmArgs &g, uint32_t *slot)
     p.out_scale = g.out_scale;
     p.out_amax = g.out_amax;
     p.ws = slot;
+    p.amax_part = g.out_amax && g.ws ? ql::ws_amax_parts(g.ws) : nullptr;
     p.a_aligned = aligned16(g.a_q) && g.lda % 16 == 0;
     p.b_aligned = aligned16(g.b_q) && g.ldb % 16 == 0;
     // Fast staging: 16-byte aligned operands whose 16-byte chunks never

@@ -374,6 +374,23 @@ __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
 }
 
 // ---------------------------------------------------------------------------
+// out_amax of a GEMM from its workgroups' maxima (|v| as FP32 bits).
+__global__ __launch_bounds__(1024) void gemm_amax_finalize(const uint32_t *parts, int64_t n, float *out)
+{
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) m = parts[i] > m ? parts[i] : m;
+    __shared__ uint32_t red[1024 / 64];
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) out[0] = __uint_as_float(m);
+}
+
+hipError_t launch_amax_finalize(const GemmParams &p, int64_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(gemm_amax_finalize, dim3(1), dim3(1024), 0, s, p.amax_part, nblocks, p.out_amax);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 __global__ void ws_fill_zero(uint32_t *ws, int64_t words)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
