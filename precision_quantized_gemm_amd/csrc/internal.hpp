@@ -24,6 +24,9 @@ constexpr int64_t WS_AMAX_PARTS = (int64_t)1 << 16;
 constexpr int64_t WS_BYTES = WS_COUNTER_BYTES + WS_PART_BYTES + WS_AMAX_PARTS * 4;
 
 inline float *ws_partials(void *ws) { return reinterpret_cast<float *>(static_cast<char *>(ws) + WS_COUNTER_BYTES); }
+// Per-tensor quantize: its workgroups' maxima at ws_amax_parts + slot *
+// QZ_PARTS_PER_SLOT (at most QZ_MAX_BLOCKS of them).
+constexpr int64_t QZ_PARTS_PER_SLOT = 1024;
 inline uint32_t *ws_amax_parts(void *ws)
 {
     return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + WS_COUNTER_BYTES + WS_PART_BYTES);
@@ -60,6 +63,10 @@ struct QzParams {
     int64_t hist_len, ring_idx;
     int margin;
     float *scale_used;
+    // Current scaling: workgroup w of the amax pass stores its maximum at
+    // amax_part[w] and a one-workgroup kernel publishes amax and the step
+    // (null: the last-workgroup election).
+    uint32_t *amax_part;
 };
 
 // Up to two whole-tensor quantizes in one launch per pass (grid row y

@@ -101,16 +101,19 @@ ql_status check_quantize(const void *x, int x_dt, int64_t rows, int64_t cols, in
     return QL_OK;
 }
 
+// ws: the caller's workspace (NULL for per-row); slot: this tensor's counter
+// slot and block of per-workgroup maxima in it.
 ql::QzParams make_qz(const void *x, int x_dt, int64_t rows, int64_t cols, int64_t ldx, int gran, int fmt,
                      const float *scale_in, void *x_q, int64_t ldq, float *scale_out, float *amax_out,
-                     uint32_t *slot)
+                     void *ws, int64_t slot)
 {
     ql::QzParams p{};
     p.x = x; p.rows = rows; p.cols = cols; p.ldx = ldx;
     p.xq = x_q; p.ldq = ldq;
     p.scale_out = scale_out; p.amax_out = amax_out;
     p.scale_src = scale_in ? scale_in : scale_out;
-    p.ws = slot;
+    p.ws = ws ? ql::ws_slot(ws, slot) : nullptr;
+    p.amax_part = ws && gran == QL_PER_TENSOR ? ql::ws_amax_parts(ws) + slot * ql::QZ_PARTS_PER_SLOT : nullptr;
     p.qmax = fmt_qmax(fmt);
     p.floor = fmt_floor(fmt);
     p.n_elems = rows * cols;
@@ -252,8 +255,8 @@ ql_status ql_quantize(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, 
 {
     ql_status st = check_quantize(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, ws);
     if (st != QL_OK) return st;
-    uint32_t *slot = ws ? ql::ws_slot(ws, ql::WS_SLOT_QA) : nullptr;
-    ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, amax_out, slot);
+    ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, gran, fmt, scale_in, x_q, ldq, scale_out, amax_out, ws,
+                             ql::WS_SLOT_QA);
     return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
@@ -275,7 +278,7 @@ ql_status ql_quantize_ring(const void *x, ql_dtype x_dt, int64_t rows, int64_t c
     ql_status st = check_quantize(x, x_dt, rows, cols, ldx, QL_PER_TENSOR, fmt, scale_in, x_q, ldq, nullptr, ws);
     if (st != QL_OK) return st;
     ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, QL_PER_TENSOR, fmt, scale_in, x_q, ldq, nullptr, amax_out,
-                             ql::ws_slot(ws, ql::WS_SLOT_QA));
+                             ws, ql::WS_SLOT_QA);
     p.ring = ring;
     p.hist_len = hist_len;
     p.ring_idx = idx;
@@ -327,9 +330,9 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     ql::QzParams px = make_qz(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, amax_x,
-                              ql::ws_slot(ws, ql::WS_SLOT_QA));
+                              ws, ql::WS_SLOT_QA);
     ql::QzParams pw = make_qz(w, x_dt, N, K, K, QL_PER_TENSOR, fmt, sw_in, w_q, K, sw, amax_w,
-                              ql::ws_slot(ws, ql::WS_SLOT_QB));
+                              ws, ql::WS_SLOT_QB);
     // x and w share each pass's launch (one grid row each).
     const hipError_t e = ql::launch_quantize_pair(px, pw, x_dt, fmt, s);
     if (e != hipSuccess) return hip_status(e, "linear_forward: quantize x and w");
@@ -348,7 +351,7 @@ ql_status ql_quantize_groups(const void *x, ql_dtype x_dt, int64_t rows, int64_t
     if ((rows + group_rows - 1) / group_rows > 0x7FFFFFFF)
         return fail(QL_ERR_UNSUPPORTED, "quantize_groups: at most 2^31-1 groups");
     ql::QzParams p = make_qz(x, x_dt, rows, cols, ldx, QL_PER_ROW, fmt, scale_in, x_q, ldq, scale_out, amax_out,
-                             nullptr);
+                             nullptr, 0);
     p.group_rows = group_rows;
     return hip_status(ql::launch_quantize(p, x_dt, fmt, static_cast<hipStream_t>(stream)), "quantize_groups launch");
 }
@@ -417,7 +420,7 @@ ql_status ql_linear_forward_static(const void *x, ql_dtype x_dt, int64_t M, int6
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     ql::QzParams px = make_qz(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, amax_x,
-                              ql::ws_slot(ws, ql::WS_SLOT_QA));
+                              ws, ql::WS_SLOT_QA);
     hipError_t e = ql::launch_quantize(px, x_dt, fmt, s);
     if (e != hipSuccess) return hip_status(e, "linear_forward_static: quantize x");
     ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
@@ -478,7 +481,7 @@ ql_status ql_linear_backward(const void *g, int64_t M, int64_t N,
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gemms) {
         ql::QzParams pg = make_qz(g, QL_DT_BF16, M, N, N, QL_PER_TENSOR, g_fmt, sg_in, g_q, N, sg, amax_g,
-                                  ql::ws_slot(ws, ql::WS_SLOT_QA));
+                                  ws, ql::WS_SLOT_QA);
         hipError_t e = ql::launch_quantize(pg, QL_DT_BF16, g_fmt, s);
         if (e != hipSuccess) return hip_status(e, "linear_backward: quantize g");
         if (want_dx) {

@@ -32,6 +32,12 @@ namespace ql {
 // keeps the end-of-grid election to 256 atomic pairs.
 constexpr int QZ_THREADS = 1024;
 constexpr int QZ_MAX_BLOCKS = 256;
+static_assert(QZ_MAX_BLOCKS <= QZ_PARTS_PER_SLOT, "one workspace maximum per workgroup");
+// Whole-tensor amax passes of at least this many workgroups publish through
+// per-workgroup maxima and a one-workgroup kernel rather than the
+// last-workgroup election, whose acquire-release atomics write back and
+// invalidate each XCD's L2.
+constexpr int QZ_PARTS_MIN_BLOCKS = 64;
 // Per-row / row-group kernel: one workgroup of 4 waves per group of rows.
 constexpr int QZ_ROW_THREADS = 256;
 constexpr int QZ_UNIT = 16;            // elements per vector unit
@@ -197,7 +203,8 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_amax(QzPack pk)
     m = block_max_u32(m, red);
     if (threadIdx.x == 0) {
         uint32_t bits;
-        if (elect_last_max_n(p.ws, m, &bits, gridDim.x)) publish(p, bits, 0);
+        if (p.amax_part) p.amax_part[blockIdx.x] = m;
+        else if (elect_last_max_n(p.ws, m, &bits, gridDim.x)) publish(p, bits, 0);
     }
 }
 
@@ -408,6 +415,18 @@ static int blocks_for(int64_t work)
     return (int)b;
 }
 
+// Publishes amax and the step of grid row y's tensor from the amax pass's
+// nblocks workgroup maxima.
+__global__ __launch_bounds__(1024) void qz_publish_parts(QzPack pk, int nblocks)
+{
+    const QzParams &p = pk.t[blockIdx.y];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nblocks; i += 1024) m = p.amax_part[i] > m ? p.amax_part[i] : m;
+    __shared__ uint32_t red[1024 / 64];
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) publish(p, m, 0);
+}
+
 static int64_t tensor_work(const QzParams &p, int mode)
 {
     return mode == MODE_SCALAR ? p.n_elems : (p.n_units > 0 ? p.n_units : p.n_elems);
@@ -416,15 +435,21 @@ static int64_t tensor_work(const QzParams &p, int mode)
 // ntensors (1 or 2) whole-tensor quantizes of the same mode and kind
 // (current or delayed scaling), grid row y on tensor y.
 template <typename T, int FMT, int MODE>
-static hipError_t launch_tensor_pack(const QzPack &pk, int ntensors, hipStream_t s)
+static hipError_t launch_tensor_pack(const QzPack &pk_in, int ntensors, hipStream_t s)
 {
-    int64_t work = tensor_work(pk.t[0], MODE);
-    if (ntensors > 1 && tensor_work(pk.t[1], MODE) > work) work = tensor_work(pk.t[1], MODE);
+    int64_t work = tensor_work(pk_in.t[0], MODE);
+    if (ntensors > 1 && tensor_work(pk_in.t[1], MODE) > work) work = tensor_work(pk_in.t[1], MODE);
     const dim3 grid(blocks_for(work), ntensors);
+    // Small grids keep the election: a few atomics cost less than the
+    // publishing launch.
+    QzPack pk = pk_in;
+    if (grid.x < QZ_PARTS_MIN_BLOCKS) pk.t[0].amax_part = pk.t[1].amax_part = nullptr;
     if (pk.t[0].delayed) {
         hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), grid, dim3(QZ_THREADS), 0, s, pk);
     } else {
         hipLaunchKernelGGL((qz_amax<T, MODE>), grid, dim3(QZ_THREADS), 0, s, pk);
+        if (pk.t[0].amax_part)
+            hipLaunchKernelGGL(qz_publish_parts, dim3(1, ntensors), dim3(1024), 0, s, pk, (int)grid.x);
         hipLaunchKernelGGL((qz_cast<T, FMT, MODE, false>), grid, dim3(QZ_THREADS), 0, s, pk);
     }
     return hipGetLastError();
@@ -462,7 +487,7 @@ template <typename T, int FMT>
 static hipError_t launch_pair_fmt(const QzParams &p0, const QzParams &p1, hipStream_t s)
 {
     const bool pack = !p0.per_row && !p1.per_row && p0.mode == p1.mode && p0.delayed == p1.delayed && !p0.ring &&
-                      !p1.ring;
+                      !p1.ring && (p0.amax_part != nullptr) == (p1.amax_part != nullptr);
     if (!pack) {
         const hipError_t e = launch_fmt<T, FMT>(p0, s);
         return e != hipSuccess ? e : launch_fmt<T, FMT>(p1, s);
