@@ -268,6 +268,10 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzPack pk)
         __shared__ uint32_t last_bits;
         __shared__ int is_last;
         m = block_max_u32(m, red);
+        if (p.amax_part) {                                  // published by qz_publish_parts
+            if (threadIdx.x == 0) p.amax_part[blockIdx.x] = m;
+            return;
+        }
         if (threadIdx.x == 0) {
             uint32_t bits = 0;
             const bool last = elect_last_max_n(p.ws, m, &bits, gridDim.x);
@@ -415,8 +419,9 @@ static int blocks_for(int64_t work)
     return (int)b;
 }
 
-// Publishes amax and the step of grid row y's tensor from the amax pass's
-// nblocks workgroup maxima.
+// Publishes grid row y's tensor from the nblocks workgroup maxima of its
+// amax pass (current scaling: amax and the step) or of its measuring cast
+// (delayed scaling: amax and the measured step, or the ring update).
 __global__ __launch_bounds__(1024) void qz_publish_parts(QzPack pk, int nblocks)
 {
     const QzParams &p = pk.t[blockIdx.y];
@@ -424,7 +429,8 @@ __global__ __launch_bounds__(1024) void qz_publish_parts(QzPack pk, int nblocks)
     for (int i = threadIdx.x; i < nblocks; i += 1024) m = p.amax_part[i] > m ? p.amax_part[i] : m;
     __shared__ uint32_t red[1024 / 64];
     m = block_max_u32(m, red);
-    if (threadIdx.x == 0) publish(p, m, 0);
+    if (p.ring) ring_publish(p, m, red);                 // block-uniform branch
+    else if (threadIdx.x == 0) publish(p, m, 0);
 }
 
 static int64_t tensor_work(const QzParams &p, int mode)
@@ -446,6 +452,8 @@ static hipError_t launch_tensor_pack(const QzPack &pk_in, int ntensors, hipStrea
     if (grid.x < QZ_PARTS_MIN_BLOCKS) pk.t[0].amax_part = pk.t[1].amax_part = nullptr;
     if (pk.t[0].delayed) {
         hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), grid, dim3(QZ_THREADS), 0, s, pk);
+        if (pk.t[0].amax_part)
+            hipLaunchKernelGGL(qz_publish_parts, dim3(1, ntensors), dim3(1024), 0, s, pk, (int)grid.x);
     } else {
         hipLaunchKernelGGL((qz_amax<T, MODE>), grid, dim3(QZ_THREADS), 0, s, pk);
         if (pk.t[0].amax_part)
