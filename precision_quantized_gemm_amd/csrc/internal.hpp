@@ -156,6 +156,10 @@ inline void finish_groups(GemmParams &p)
 // p.amax_part (run right after the GEMM on the same stream).
 hipError_t launch_amax_finalize(const GemmParams &p, int64_t nblocks, hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails), the size of a persistent grid of one workgroup per CU.
+int device_cu_count();
+
 // a_fmt / b_fmt: FMT_*; a_mn / b_mn: operand stored MN-major.
 hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s);
 

@@ -135,11 +135,14 @@ __device__ __forceinline__ void gemm_publish_amax(const GemmParams &p, uint32_t 
     }
 }
 
-// Linear workgroup id -> (tile_m, tile_n): XCD-contiguous, then grouped.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn)
+// Linear tile id -> (tile_m, tile_n): XCD-contiguous, then grouped.  Ids
+// that are equal mod 8 run on one XCD when the launch hands consecutive
+// workgroups to consecutive XCDs (a persistent grid must be a multiple of 8
+// for its ids id, id + grid, ... to keep that property).
+__device__ __forceinline__ void tile_coords_of(int id, int tiles_m, int tiles_n, int &tm, int &tn)
 {
     const int total = tiles_m * tiles_n;
-    int t = blockIdx.x;
+    int t = id;
     if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
     const int per_group = GEMM_GM * tiles_n;
     const int first_m = (t / per_group) * GEMM_GM;
@@ -147,6 +150,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
     const int in_group = t - (t / per_group) * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    tile_coords_of((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
 }
 
 }  // namespace ql

@@ -36,6 +36,14 @@
 // as the first operand): then each lane's register quad holds 4
 // consecutive output columns of one row, which the epilogue moves through
 // LDS with 16-byte writes.
+//
+// The grid is persistent when K is a whole number of steps: one workgroup
+// per CU walks tiles id, id + grid, ...  When a tile's epilogue stays in registers (whole tile, per-tensor
+// scales, 16-byte aligned rows) and K is an even number of whole steps, the
+// two refills past its last step fetch the next tile's first two steps
+// instead of nothing, and the last step reads the next tile's first
+// fragments.  The next tile's start-up latency then hides behind this
+// tile's epilogue, and no workgroup launch separates the two.
 #pragma once
 
 #include "qgemm_common.hpp"
@@ -183,9 +191,10 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
     return vmax;
 }
 
-template <int AF, int BF, bool KTAIL>
+template <int AF, int BF, bool KTAIL, bool CHAIN>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 {
+    static_assert(!(CHAIN && KTAIL), "a chained grid needs whole k-steps");
     typedef Mma32<BF, AF> MMA;                 // operands swapped: acc holds C^T
     static_assert(AF != FMT_INT8 && BF != FMT_INT8, "the pipelined kernel is FP8 only");
     constexpr int RPS = NT_READS_PER_SLOT;
@@ -194,20 +203,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NT_STAGES * NT_STAGE_BYTES];
     __shared__ uint32_t red[GEMM_THREADS / 64];
 
-    int tm, tn;
-    tile_coords(p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * NT_BM, n0 = (int64_t)tn * NT_BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar LDS windows
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const int total = p.tiles_m * p.tiles_n;
 
-    // Buffer resources from the tile's first row; rows past the matrix are
-    // outside num_records and load as zeros.
-    const int64_t a_rows = p.M - m0, b_rows = p.N - n0;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.a + m0 * p.lda), (short)0, (int)(a_rows > 0 ? a_rows * p.lda : 0), BUF_WORD3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.b + n0 * p.ldb), (short)0, (int)(b_rows > 0 ? b_rows * p.ldb : 0), BUF_WORD3);
+    // A tile's operand panels start at its first rows; rows past the
+    // matrix are outside num_records and load as zeros.  The loop carries
+    // base and size as plain scalars and each step builds the buffer
+    // resources from them (a resource carried through the loop would be
+    // treated as divergent).
+    auto panel_bytes = [&](int64_t ld, int64_t rows_left) { return (int)(rows_left > 0 ? rows_left * ld : 0); };
 
     // LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB
     // each, so a fragment read's stage and fragment offsets fit the
@@ -232,17 +238,23 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 
     const int K32 = (int)p.K;
     const int nk = (int)((p.K + NT_BK - 1) / NT_BK);
+    __builtin_assume(nk > 0);   // K == 0 never reaches this kernel
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
     const uint32_t lds_wave = lds_base + (uint32_t)wave * 1024u;   // wave-uniform: lands in M0
-    // Direct-to-LDS load j (0 .. NT_LOADS-1) of the step at k offset k0 into
-    // stage S.  Without a K tail every step is whole and k0 rides in the
-    // scalar offset.  With one (KTAIL), chunks at or past K get an offset
-    // outside the buffer range and load as zeros, which also covers the
-    // refills past the last step.
-    auto issue_one = [&](auto S, int k0, int j) {
+    // Direct-to-LDS load j (0 .. NT_LOADS-1) of the step at k offset k0 of
+    // the panels (ra, rb) into stage S.  Without a K tail every step is
+    // whole and k0 rides in the scalar offset.  With one (KTAIL), chunks at
+    // or past K get an offset outside the buffer range and load as zeros,
+    // which also covers the refills past the last step.
+    auto issue_one = [&](auto S, int k0, int j, const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb) {
         constexpr int STAGE = decltype(S)::value;
         const bool is_a = j < NT_LOADS / 2;
-        const lds_ptr_t dst = (lds_ptr_t)(uintptr_t)(lds_wave + (uint32_t)((is_a ? 0 : NT_STAGES * NT_A_BYTES) +
+        // The window base goes through an empty asm so each load adds its
+        // constant in place (one scalar add) instead of the compiler keeping
+        // 16 precomputed bases live, which the tile loop cannot afford.
+        uint32_t wbase = lds_wave;
+        asm volatile("" : "+s"(wbase));
+        const lds_ptr_t dst = (lds_ptr_t)(uintptr_t)(wbase + (uint32_t)((is_a ? 0 : NT_STAGES * NT_A_BYTES) +
                                                                  STAGE * NT_A_BYTES + (j % (NT_LOADS / 2)) * 4096));
         if constexpr (!KTAIL) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, dst, 16, (int)goff[j], k0, 0, 0);
@@ -257,10 +269,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     auto refill_k = [&](int step) { return (KTAIL || step < nk ? step : nk - 1) * NT_BK; };
 
     acc_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
 
     const int lr = lane & 31, h = lane >> 5;
     // Per-lane read bases: a lane reads rows (wm0 | wn0) + f*32 + lr, and
@@ -295,153 +303,200 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         MMA::run(acc[i][j], f[2 * (TM + j)], f[2 * (TM + j) + 1], f[2 * i], f[2 * i + 1]);
     };
 
-    // One k-step worked from stage S (= kt % 2).  Half 0: MFMAs on set 0
-    // while half 1's fragments are read into set 1 (front-loaded,
-    // NT_READS_PER_SLOT per MFMA slot).  Then this wave is done with stage S;
-    // once all waves pass the barrier, everyone's loads of step kt+1 have
-    // landed.  Half 1: MFMAs on set 1 while step kt+1's half-0 fragments are
-    // read from the other stage into set 0 and stage S is refilled with step
-    // kt+2 (one load per slot: bursts overflow the texture address queue and
-// stall the wave).
-    auto step = [&](auto S, int kt) {
-        constexpr int STAGE = decltype(S)::value;
-        typedef std::integral_constant<int, 1 - STAGE> SN;
-        nt_unroll<0, 16>([&](auto T) {
-            constexpr int t = decltype(T)::value;
-            mma(f0, t);
-            nt_unroll<0, RPS>([&](auto R) {
-                constexpr int r = t * RPS + decltype(R)::value;
-                if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
-            });
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        nt_wait_parts(f1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __builtin_amdgcn_s_barrier();
-        const int k_refill = refill_k(kt + 2);
-        nt_unroll<0, 16>([&](auto T) {
-            constexpr int t = decltype(T)::value;
-            mma(f1, t);
-            nt_unroll<0, RPS>([&](auto R) {
-                constexpr int r = t * RPS + decltype(R)::value;
-                if constexpr (r < 16) f0[r] = read_frag(SN{}, I0{}, std::integral_constant<int, r>{});
-            });
-            issue_one(S, k_refill, t);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        nt_wait_parts(f0);
-    };
-
-    if (nk > 0) {
-#pragma unroll
-        for (int j = 0; j < NT_LOADS; ++j) issue_one(I0{}, 0, j);
-        if (nk > 1) {
-#pragma unroll
-            for (int j = 0; j < NT_LOADS; ++j) issue_one(I1{}, NT_BK, j);
-            __builtin_amdgcn_s_waitcnt(VM_ONE_STEP);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
-        __builtin_amdgcn_s_barrier();
-        nt_unroll<0, 16>([&](auto T) { f0[decltype(T)::value] = read_frag(I0{}, I0{}, T); });
-        nt_wait_parts(f0);
-    }
-    // Steps past the end read stale fragments that no MFMA uses; the loop
-    // runs two steps per iteration so each step's stage is a constant.
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(I0{}, kt);
-        if (kt + 1 < nk) step(I1{}, kt + 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-
-    // Epilogue.  Block (i, j) holds C^T: element r of lane l is output row
-    // i*32 + l%32, column j*32 + (r/4)*8 + 4*(l/32) + r%4.
-    //
-    // Fast path (whole tile inside the output, per-tensor scales, 16-byte
-    // aligned output and bias rows): straight from registers.  Swapping the
-    // upper half-wave of register quads 0 and 1 with the lower half-wave of
-    // quads 2 and 3 (v_permlane32_swap) leaves lane l with the 16
-    // consecutive columns 16*(l/32) .. +15 of its row, in quad order
-    // 0, 2, 1, 3, which then go out as 16-byte stores.
-    //
-    // Otherwise through LDS, one 32-row slab of the wave tile at a time:
-    // register quad q goes to LDS as one 16-byte write, then each lane takes
-    // 4 columns at a time through the general epilogue with its bounds
-    // checks.  With row stride EP_LD = 132 words, the 16 lanes that share an
-    // LDS clock touch 16 distinct bank slots.
-    Epilogue epi(p);
-    const bool fast_epi = epi.per_tensor && p.out_vec16 && p.bias_vec16 && m0 + NT_BM <= p.M && n0 + NT_BN <= p.N;
+    // CHAIN (the launcher guarantees: every tile whole, the register
+    // epilogue, an even number of whole k-steps): the next tile's first two
+    // steps are fetched by this tile's last refills, since the epilogue
+    // leaves the LDS stages alone and the next tile starts on stage 0.
     uint32_t vmax = 0;
-    if (fast_epi) {
-        // One block per iteration at run time (keeps the code and register
-        // pressure small); the block's accumulators are picked out through
-        // compile-time indices.
-#pragma unroll 1
-        for (int b = 0; b < TM * TN; ++b) {
-            const int i = b / TN, j = b % TN;
-            uint32_t x[16];
-            nt_unroll<0, TM * TN>([&](auto B) {
-                constexpr int bb = decltype(B)::value;
-                if (b == bb) {
+    bool started = false;   // this tile's steps 0 and 1 are in flight and f0 holds its first fragments
+    // The panels refills load from (this tile's, then the next one's).
+    const uint8_t *pa = p.a, *pb = p.b;
+    int na = 0, nb = 0;
+
+    // Without CHAIN the body runs once (one tile per workgroup).
+    int id = (int)blockIdx.x;
+    do {
+        int tm, tn;
+        tile_coords_of(id, p.tiles_m, p.tiles_n, tm, tn);
+        const int64_t m0 = (int64_t)tm * NT_BM, n0 = (int64_t)tn * NT_BN;
+        const bool whole = CHAIN || (m0 + NT_BM <= p.M && n0 + NT_BN <= p.N);
+        const int next = id + (int)gridDim.x;
+        const bool chain = CHAIN && next < total;
+
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = MMA::bits(acc[bb / TN][bb % TN], r);
-                }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
+
+        // One k-step worked from stage S (= kt % 2).  Half 0: MFMAs on set 0
+        // while half 1's fragments are read into set 1 (front-loaded,
+        // NT_READS_PER_SLOT per MFMA slot).  Then this wave is done with
+        // stage S; once all waves pass the barrier, everyone's loads of step
+        // kt+1 have landed.  Half 1: MFMAs on set 1 while step kt+1's half-0
+        // fragments are read from the other stage into set 0 and stage S is
+        // refilled with step kt+2 -- of the next tile when chaining past the
+        // end (one load per slot: bursts overflow the texture address queue
+        // and stall the wave).
+        auto step = [&](auto S, int kt) {
+            constexpr int STAGE = decltype(S)::value;
+            typedef std::integral_constant<int, 1 - STAGE> SN;
+            nt_unroll<0, 16>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                mma(f0, t);
+                nt_unroll<0, RPS>([&](auto R) {
+                    constexpr int r = t * RPS + decltype(R)::value;
+                    if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
             });
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const auto s02 = __builtin_amdgcn_permlane32_swap(x[r], x[8 + r], false, false);
-                x[r] = s02[0]; x[8 + r] = s02[1];
-                const auto s13 = __builtin_amdgcn_permlane32_swap(x[4 + r], x[12 + r], false, false);
-                x[4 + r] = s13[0]; x[12 + r] = s13[1];
+            nt_wait_parts(f1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __builtin_amdgcn_s_barrier();
+            const bool to_next = chain && kt + 2 >= nk;
+            if (chain && kt + 2 == nk) {
+                int tm2, tn2;
+                tile_coords_of(next, p.tiles_m, p.tiles_n, tm2, tn2);
+                const int64_t m2 = (int64_t)tm2 * NT_BM, n2 = (int64_t)tn2 * NT_BN;
+                pa = p.a + m2 * p.lda; na = panel_bytes(p.lda, p.M - m2);
+                pb = p.b + n2 * p.ldb; nb = panel_bytes(p.ldb, p.N - n2);
             }
-            const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
-                                make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
-            const int64_t row = m0 + wm0 + i * 32 + lr;
-            const int64_t col = n0 + wn0 + j * 32 + h * 16;
-            vmax = nt_store16(p, epi, w, row, col, vmax);
-        }
-    } else {
-        constexpr int EP_LD = WN + 4;                    // padded row, in words
-        uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 32 * EP_LD;
-        // The slab loop runs at run time (its body is large); the accumulator
-        // rows go to LDS through compile-time indices so they stay in
-        // registers.
-#pragma unroll 1
-        for (int i = 0; i < TM; ++i) {
-            __syncthreads();
-            nt_unroll<0, TM>([&](auto I) {
-                constexpr int ii = decltype(I)::value;
-                if (i == ii) {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
-                                make_uint4(MMA::bits(acc[ii][j], 4 * q), MMA::bits(acc[ii][j], 4 * q + 1),
-                                           MMA::bits(acc[ii][j], 4 * q + 2), MMA::bits(acc[ii][j], 4 * q + 3));
-                }
+            const __amdgpu_buffer_rsrc_t la = __builtin_amdgcn_make_buffer_rsrc((void *)pa, (short)0, na, BUF_WORD3);
+            const __amdgpu_buffer_rsrc_t lb = __builtin_amdgcn_make_buffer_rsrc((void *)pb, (short)0, nb, BUF_WORD3);
+            const int k_refill = to_next ? (kt + 2 - nk) * NT_BK : refill_k(kt + 2);
+            nt_unroll<0, 16>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                mma(f1, t);
+                nt_unroll<0, RPS>([&](auto R) {
+                    constexpr int r = t * RPS + decltype(R)::value;
+                    if constexpr (r < 16) f0[r] = read_frag(SN{}, I0{}, std::integral_constant<int, r>{});
+                });
+                issue_one(S, k_refill, t, la, lb);
+                __builtin_amdgcn_sched_barrier(0);
             });
+            nt_wait_parts(f0);
+        };
+
+        if (!started) {
+            pa = p.a + m0 * p.lda; na = panel_bytes(p.lda, p.M - m0);
+            pb = p.b + n0 * p.ldb; nb = panel_bytes(p.ldb, p.N - n0);
+            const __amdgpu_buffer_rsrc_t la = __builtin_amdgcn_make_buffer_rsrc((void *)pa, (short)0, na, BUF_WORD3);
+            const __amdgpu_buffer_rsrc_t lb = __builtin_amdgcn_make_buffer_rsrc((void *)pb, (short)0, nb, BUF_WORD3);
+            __syncthreads();   // the previous tile's LDS epilogue is done with the stages
+#pragma unroll
+            for (int j = 0; j < NT_LOADS; ++j) issue_one(I0{}, 0, j, la, lb);
+            if (nk > 1) {
+#pragma unroll
+                for (int j = 0; j < NT_LOADS; ++j) issue_one(I1{}, NT_BK, j, la, lb);
+                __builtin_amdgcn_s_waitcnt(VM_ONE_STEP);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
+            __builtin_amdgcn_s_barrier();
+            nt_unroll<0, 16>([&](auto T) { f0[decltype(T)::value] = read_frag(I0{}, I0{}, T); });
+            nt_wait_parts(f0);
+        }
+        // Steps past the end read stale fragments that no MFMA uses (or,
+        // chaining, the next tile's first ones); the loop runs two steps per
+        // iteration so each step's stage is a constant.
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(I0{}, kt);
+            if (kt + 1 < nk) step(I1{}, kt + 1);
+        }
+        if (!chain) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
-            constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
+        }
+        started = chain;
+
+        // Epilogue.  Block (i, j) holds C^T: element r of lane l is output row
+        // i*32 + l%32, column j*32 + (r/4)*8 + 4*(l/32) + r%4.
+        //
+        // Fast path (whole tile inside the output, per-tensor scales, 16-byte
+        // aligned output and bias rows): straight from registers.  Swapping the
+        // upper half-wave of register quads 0 and 1 with the lower half-wave of
+        // quads 2 and 3 (v_permlane32_swap) leaves lane l with the 16
+        // consecutive columns 16*(l/32) .. +15 of its row, in quad order
+        // 0, 2, 1, 3, which then go out as 16-byte stores.
+        //
+        // Otherwise through LDS, one 32-row slab of the wave tile at a time:
+        // register quad q goes to LDS as one 16-byte write, then each lane takes
+        // 4 columns at a time through the general epilogue with its bounds
+        // checks.  With row stride EP_LD = 132 words, the 16 lanes that share an
+        // LDS clock touch 16 distinct bank slots.
+        const GemmParams &pe = p;
+        const Epilogue epi(pe);
+        if (CHAIN || (epi.per_tensor && p.out_vec16 && p.bias_vec16 && whole)) {
+            // One block per iteration at run time (keeps the code and register
+            // pressure small); the block's accumulators are picked out through
+            // compile-time indices.
 #pragma unroll 1
-            for (int g = 0; g < PER_LANE; g += GROUP) {
-                uint4 w[GROUP];
+            for (int b = 0; b < TM * TN; ++b) {
+                const int i = b / TN, j = b % TN;
+                uint32_t x[16];
+                nt_unroll<0, TM * TN>([&](auto B) {
+                    constexpr int bb = decltype(B)::value;
+                    if (b == bb) {
 #pragma unroll
-                for (int u = 0; u < GROUP; ++u) {
-                    const int idx = lane + (g + u) * 64;
-                    w[u] = *reinterpret_cast<const uint4 *>(ep + (idx / C4) * EP_LD + (idx % C4) * 4);
+                        for (int r = 0; r < 16; ++r) x[r] = MMA::bits(acc[bb / TN][bb % TN], r);
+                    }
+                });
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto s02 = __builtin_amdgcn_permlane32_swap(x[r], x[8 + r], false, false);
+                    x[r] = s02[0]; x[8 + r] = s02[1];
+                    const auto s13 = __builtin_amdgcn_permlane32_swap(x[4 + r], x[12 + r], false, false);
+                    x[4 + r] = s13[0]; x[12 + r] = s13[1];
                 }
+                const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
+                                    make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
+                const int64_t row = m0 + wm0 + i * 32 + lr;
+                const int64_t col = n0 + wn0 + j * 32 + h * 16;
+                vmax = nt_store16(pe, epi, w, row, col, vmax);
+            }
+        } else if constexpr (!CHAIN) {
+            constexpr int EP_LD = WN + 4;                    // padded row, in words
+            uint32_t *ep = reinterpret_cast<uint32_t *>(lds) + wave * 32 * EP_LD;
+            // The slab loop runs at run time (its body is large); the accumulator
+            // rows go to LDS through compile-time indices so they stay in
+            // registers.
+#pragma unroll 1
+            for (int i = 0; i < TM; ++i) {
+                __syncthreads();
+                nt_unroll<0, TM>([&](auto I) {
+                    constexpr int ii = decltype(I)::value;
+                    if (i == ii) {
 #pragma unroll
-                for (int u = 0; u < GROUP; ++u) {
-                    const int idx = lane + (g + u) * 64;
-                    const int64_t row = m0 + wm0 + i * 32 + idx / C4;
-                    const int64_t col = n0 + wn0 + (idx % C4) * 4;
-                    if (row < p.M && col < p.N) vmax = epi.store4<MMA::INT_ACC>(w[u], row, col, vmax);
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                *reinterpret_cast<uint4 *>(ep + lr * EP_LD + j * 32 + q * 8 + h * 4) =
+                                    make_uint4(MMA::bits(acc[ii][j], 4 * q), MMA::bits(acc[ii][j], 4 * q + 1),
+                                               MMA::bits(acc[ii][j], 4 * q + 2), MMA::bits(acc[ii][j], 4 * q + 3));
+                    }
+                });
+                __syncthreads();
+                constexpr int C4 = WN / 4, PER_LANE = 32 * C4 / 64, GROUP = 8;
+#pragma unroll 1
+                for (int g = 0; g < PER_LANE; g += GROUP) {
+                    uint4 w[GROUP];
+#pragma unroll
+                    for (int u = 0; u < GROUP; ++u) {
+                        const int idx = lane + (g + u) * 64;
+                        w[u] = *reinterpret_cast<const uint4 *>(ep + (idx / C4) * EP_LD + (idx % C4) * 4);
+                    }
+#pragma unroll
+                    for (int u = 0; u < GROUP; ++u) {
+                        const int idx = lane + (g + u) * 64;
+                        const int64_t row = m0 + wm0 + i * 32 + idx / C4;
+                        const int64_t col = n0 + wn0 + (idx % C4) * 4;
+                        if (row < pe.M && col < pe.N) vmax = epi.store4<MMA::INT_ACC>(w[u], row, col, vmax);
+                    }
                 }
             }
         }
-    }
+        if constexpr (!CHAIN) break;
+        id = next;
+    } while (id < total);
     if (p.out_amax) gemm_publish_amax(p, vmax, red);
 }
 
@@ -450,12 +505,22 @@ hipError_t launch_nt(GemmParams p, hipStream_t s)
 {
     p.tiles_m = (int)((p.M + NT_BM - 1) / NT_BM);
     p.tiles_n = (int)((p.N + NT_BN - 1) / NT_BN);
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    // Chained (persistent: one workgroup per CU -- its LDS and registers
+    // allow no more -- each walking every grid-th tile) when every tile is
+    // whole, takes the register epilogue, and K is an even number of whole
+    // steps; otherwise one tile per workgroup.
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t cus = device_cu_count();
+    const bool chain = p.M % NT_BM == 0 && p.N % NT_BN == 0 && p.K % (2 * NT_BK) == 0 && p.sa_group == 0 &&
+                       p.sb_group == 0 && p.out_vec16 && p.bias_vec16 && tiles > cus;
+    const int64_t grid = chain ? cus : tiles;
     if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
-    if (p.K % NT_BK == 0)
-        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
+    if (chain)
+        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false, true>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
+    else if (p.K % NT_BK == 0)
+        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false, false>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, true>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
+        hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, true, false>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.out_amax || !p.amax_part) return e;
     return launch_amax_finalize(p, grid, s);

@@ -6,6 +6,7 @@
 // format; the cuda kernels raise TypeError for a wrong dtype; mm_fp8 raises
 // ValueError for an unknown out_dtype).  Then it picks a kernel instance by
 // format, layout and alignment and launches on the caller's stream.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
@@ -31,6 +32,20 @@ hipError_t launch_qgemm(const GemmParams &pp, int a_fmt, int b_fmt, int a_mn, in
                                                     : launch_qgemm_e4m3_e5m2(p, a_mn, b_mn, s);
     return b_fmt == FMT_E4M3 ? launch_qgemm_e5m2_e4m3(p, a_mn, b_mn, s)
                              : launch_qgemm_e5m2_e5m2(p, a_mn, b_mn, s);
+}
+
+int device_cu_count()
+{
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 }  // namespace ql
 

@@ -423,3 +423,49 @@ def test_direct_lds_degenerate():
                         a_layout="mn_major", b_layout="mn_major", out_dtype="bf16", out_amax=True, K=K)
     torch.cuda.synchronize()
     assert out.shape == (32, 0) and amax.item() == 0.0
+
+
+@pytest.mark.parametrize("K,out_dtype,bias_kind,af,bf", [(256, "bf16", "fp32", 0, 0), (768, "fp32", "bf16", 1, 0),
+                                                        (256, "e4m3", None, 0, 0), (512, "e4m3", "fp32", 0, 1)])
+def test_pipelined_chained_grid(orc, K, out_dtype, bias_kind, af, bf):
+    """Every tile whole, per-tensor scales, 16-byte rows and an even number
+    of whole k-steps: the pipelined kernel runs one workgroup per CU, each
+    walking several tiles and fetching the next tile's first two steps during
+    the current tile's last two (with K = 256 those are all of its refills).
+    Sampled entries: one in every 256 x 256 tile, full rows and columns, and
+    random ones; out_amax equals max |v| of the FP32 output of the same
+    product."""
+    M, N = 8192, 4096 + 1024
+    a = finite_codes(orc, 71, af, M, K, af)
+    b = finite_codes(orc, 72, bf, N, K, bf)
+    sa, sb = np.float32(0.01), np.float32(0.02)
+    dev = "cuda"
+    b32 = synth.normal(73, 0, N, 0.5)
+    bias_t = {"bf16": torch.from_numpy(b32).to(torch.bfloat16), "fp32": torch.from_numpy(b32), None: None}[bias_kind]
+    bias_vals = None if bias_t is None else bias_t.float().numpy()
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    ts = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)
+    tbias = None if bias_t is None else bias_t.to(dev)
+    ref32, amax32 = q.qgemm(ta, FMT[af], tb, FMT[bf], ts(sa), ts(sb), bias=tbias, out_dtype="fp32", out_amax=True)
+    torch.cuda.synchronize()
+    assert amax32.item() == ref32.abs().max().item()
+    os_ = np.float32(amax32.item() / 448.0 * 0.5) if out_dtype == "e4m3" else None
+    out, amax = q.qgemm(ta, FMT[af], tb, FMT[bf], ts(sa), ts(sb), bias=tbias, out_dtype=out_dtype,
+                        out_scale=None if os_ is None else ts(os_), out_amax=True)
+    torch.cuda.synchronize()
+    assert amax.item() == amax32.item()
+    rng = np.random.default_rng(74)
+    tm, tn = np.meshgrid(np.arange(M // 256), np.arange(N // 256), indexing="ij")
+    per_tile_m = (tm.ravel() * 256 + rng.integers(0, 256, tm.size)).astype(np.int64)
+    per_tile_n = (tn.ravel() * 256 + rng.integers(0, 256, tn.size)).astype(np.int64)
+    sm, sn = sampled_entries(M, N, rows=3, cols=3, rand=2000, seed=75)
+    ms = np.concatenate([per_tile_m, sm])
+    ns = np.concatenate([per_tile_n, sn])
+    acc, S, _, H, v, sasb = oracle_entries(orc, a, af, 0, b, bf, 0, K, ms, ns, [sa], 0, [sb], 0, bias_vals)
+    got = out_values(out.cpu())[ms, ns]
+    if out_dtype == "e4m3":
+        differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, bias=bias_of(bias_vals, ns), what="chained")
+        print("chained grid e4m3 differing codes:", differ, "of", got.size)
+    else:
+        print("chained grid", check_float(got, v, S, H, sasb, K, bias=bias_of(bias_vals, ns),
+                                          what=f"chained {out_dtype}"))
