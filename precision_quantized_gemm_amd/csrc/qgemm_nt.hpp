@@ -59,6 +59,22 @@ constexpr int NT_STAGE_BYTES = (NT_BM + NT_BN) * NT_BK;          // 64 KiB
 constexpr int NT_LOADS = NT_STAGE_BYTES / (GEMM_THREADS * 16);   // 16-byte loads per thread per step (16)
 constexpr int NT_A_BYTES = NT_BM * NT_BK;                        // one stage of A (or B): 32 KiB
 constexpr int NT_READS_PER_SLOT = 2;  // fragment reads issued per MFMA slot (front-loaded)
+// Refill schedule: the step-after-next's NT_LOADS loads go out
+// NT_LOADS_PER_SLOT per MFMA slot from slot NT_LOAD_SLOT0, counted over the
+// step's two halves (0-15 the first, 16-31 the second).  A start in the
+// first half adds a barrier there, once every wave has read the stage.
+constexpr int NT_LOAD_SLOT0 = 10;
+constexpr int NT_LOADS_PER_SLOT = 1;
+static_assert(NT_LOAD_SLOT0 >= 16 || NT_LOAD_SLOT0 * NT_READS_PER_SLOT >= 16,
+              "the refill starts only after this wave has issued every read of the stage");
+static_assert(NT_LOAD_SLOT0 + (NT_LOADS + NT_LOADS_PER_SLOT - 1) / NT_LOADS_PER_SLOT <= 32,
+              "the refill ends within the step");
+// Refill loads issued before the mid-step wait, which may stay in flight.
+constexpr int NT_REFILL_EARLY =
+    NT_LOAD_SLOT0 >= 16 ? 0
+                        : ((16 - NT_LOAD_SLOT0) * NT_LOADS_PER_SLOT < NT_LOADS ? (16 - NT_LOAD_SLOT0) * NT_LOADS_PER_SLOT
+                                                                                : NT_LOADS);
+constexpr int NT_VM_MID = 0x0F70 | (NT_REFILL_EARLY & 0xF) | ((NT_REFILL_EARLY >> 4) << 14);
 
 __device__ __forceinline__ int nt_swz(int r) { return (r >> 1) & 7; }
 
@@ -340,18 +356,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         auto step = [&](auto S, int kt) {
             constexpr int STAGE = decltype(S)::value;
             typedef std::integral_constant<int, 1 - STAGE> SN;
-            nt_unroll<0, 16>([&](auto T) {
-                constexpr int t = decltype(T)::value;
-                mma(f0, t);
-                nt_unroll<0, RPS>([&](auto R) {
-                    constexpr int r = t * RPS + decltype(R)::value;
-                    if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
-                });
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            nt_wait_parts(f1);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __builtin_amdgcn_s_barrier();
             const bool to_next = chain && kt + 2 >= nk;
             if (chain && kt + 2 == nk) {
                 int tm2, tn2;
@@ -363,6 +367,36 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
             const __amdgpu_buffer_rsrc_t la = __builtin_amdgcn_make_buffer_rsrc((void *)pa, (short)0, na, BUF_WORD3);
             const __amdgpu_buffer_rsrc_t lb = __builtin_amdgcn_make_buffer_rsrc((void *)pb, (short)0, nb, BUF_WORD3);
             const int k_refill = to_next ? (kt + 2 - nk) * NT_BK : refill_k(kt + 2);
+            // Refill loads issued in slot t of half H (NT_LOAD_SLOT0 counts
+            // slots across both halves).
+            auto refills = [&](auto H, auto T) {
+                constexpr int g = decltype(H)::value * 16 + decltype(T)::value - NT_LOAD_SLOT0;
+                if constexpr (g >= 0)
+                    nt_unroll<0, NT_LOADS_PER_SLOT>([&](auto U) {
+                        constexpr int i = g * NT_LOADS_PER_SLOT + decltype(U)::value;
+                        if constexpr (i < NT_LOADS) issue_one(S, k_refill, i, la, lb);
+                    });
+            };
+            nt_unroll<0, 16>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                mma(f0, t);
+                nt_unroll<0, RPS>([&](auto R) {
+                    constexpr int r = t * RPS + decltype(R)::value;
+                    if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
+                });
+                if constexpr (NT_LOAD_SLOT0 < 16 && t == NT_LOAD_SLOT0) {
+                    // Every wave has its fragments of stage S: it may refill.
+                    nt_wait_parts(f1);
+                    __builtin_amdgcn_s_barrier();
+                }
+                refills(I0{}, T);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // This wave's loads of step kt+1 have landed (all but the refill
+            // loads issued since); after the barrier, everyone's have.
+            nt_wait_parts(f1);
+            __builtin_amdgcn_s_waitcnt(NT_VM_MID);
+            __builtin_amdgcn_s_barrier();
             nt_unroll<0, 16>([&](auto T) {
                 constexpr int t = decltype(T)::value;
                 mma(f1, t);
@@ -370,7 +404,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                     constexpr int r = t * RPS + decltype(R)::value;
                     if constexpr (r < 16) f0[r] = read_frag(SN{}, I0{}, std::integral_constant<int, r>{});
                 });
-                issue_one(S, k_refill, t, la, lb);
+                refills(I1{}, T);
                 __builtin_amdgcn_sched_barrier(0);
             });
             nt_wait_parts(f0);
