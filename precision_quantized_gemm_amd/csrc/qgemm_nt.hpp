@@ -11,12 +11,13 @@
 // row).  Global data goes straight into LDS with buffer_load_dwordx4 ...
 // lds (no registers, no LDS write instructions).  A step is worked in two
 // 64-deep halves with two fragment register sets: half 0's MFMAs run while
-// half 1's fragments are read; then this wave is done with the stage, and
-// after the barrier (which also certifies everyone's loads of the next
-// step) half 1's MFMAs run while the next step's first fragments are read
-// and the freed stage is refilled with the step after next.  With one wave
-// per SIMD the program order is the schedule, so every MFMA slot carries
-// one LDS read and, early in half 1, two loads.  Every step has the same
+// half 1's fragments are read; once every wave holds them (a barrier part
+// way through half 0) the stage is refilled with the step after next, one
+// load per MFMA slot into half 1; after the mid-step barrier (which
+// certifies everyone's loads of the next step) half 1's MFMAs run while the
+// next step's first fragments are read.  With one wave per SIMD the program
+// order is the schedule: every MFMA slot carries up to two LDS reads and
+// one load.  Every step has the same
 // shape: steps past the end load zeros (offsets past K are out of the
 // buffer range) into a stage nobody reads.  Rows past M / N and chunks
 // past K come back as zeros through the buffer range check.
@@ -346,13 +347,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 
         // One k-step worked from stage S (= kt % 2).  Half 0: MFMAs on set 0
         // while half 1's fragments are read into set 1 (front-loaded,
-        // NT_READS_PER_SLOT per MFMA slot).  Then this wave is done with
-        // stage S; once all waves pass the barrier, everyone's loads of step
-        // kt+1 have landed.  Half 1: MFMAs on set 1 while step kt+1's half-0
-        // fragments are read from the other stage into set 0 and stage S is
-        // refilled with step kt+2 -- of the next tile when chaining past the
-        // end (one load per slot: bursts overflow the texture address queue
-        // and stall the wave).
+        // NT_READS_PER_SLOT per MFMA slot); once every wave has them (the
+        // barrier at slot NT_LOAD_SLOT0) stage S is refilled with step kt+2
+        // -- of the next tile when chaining past the end -- one load per
+        // slot (bursts overflow the texture address queue and stall the
+        // wave).  At the mid-step barrier everyone's loads of step kt+1 have
+        // landed.  Half 1: MFMAs on set 1 while step kt+1's half-0 fragments
+        // are read from the other stage into set 0, and the refill goes on.
         auto step = [&](auto S, int kt) {
             constexpr int STAGE = decltype(S)::value;
             typedef std::integral_constant<int, 1 - STAGE> SN;
