@@ -12,9 +12,14 @@
 //
 // Kernels
 //   qz_amax   per-tensor current scaling, pass 1: HBM-streaming max|x| with
-//             16-byte loads; the last workgroup publishes amax and the step.
+//             16-byte loads; on small grids the last workgroup publishes
+//             amax and the step, on large ones each workgroup leaves its
+//             maximum in the workspace.
 //   qz_cast   pass 2 (or the only pass under delayed scaling, where it also
-//             measures amax and publishes it from its last workgroup).  As
+//             measures amax and publishes it from its last workgroup, or
+//             through per-workgroup maxima and qz_publish_parts).  As pass 2
+//             after per-workgroup maxima, every workgroup reduces them and
+//             workgroup 0 publishes amax and the step.  As
 //             pass 2 it walks the tensor from the end backwards, so it
 //             starts on the data pass 1 read last, which the memory-side
 //             cache (256 MB) still holds.
@@ -217,7 +222,27 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzPack pk)
     const QzParams &p = pk.t[blockIdx.y];
     const T *x = static_cast<const T *>(p.x);
     uint8_t *xq = static_cast<uint8_t *>(p.xq);
-    const Divider div(p.scale_src[0]);
+    float step;
+    if (!MEASURE && p.amax_part) {
+        // Current scaling after an amax pass of the same grid that left one
+        // maximum per workgroup: every workgroup reduces them itself and
+        // workgroup 0 publishes amax and the step, so no launch sits between
+        // the two passes.
+        uint32_t m = 0;
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += QZ_THREADS) m = p.amax_part[i] > m ? p.amax_part[i] : m;
+        __shared__ uint32_t red0[QZ_THREADS / 64];
+        m = block_max_u32(m, red0);
+        const float a = __uint_as_float(m);
+        const float amax = a < p.floor ? p.floor : a;       // NaN stays NaN
+        step = amax / p.qmax;                                // IEEE division
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (p.amax_out) p.amax_out[0] = amax;
+            p.scale_out[0] = step;
+        }
+    } else {
+        step = p.scale_src[0];
+    }
+    const Divider div(step);
     const int64_t gtid = (int64_t)blockIdx.x * QZ_THREADS + threadIdx.x;
     const int64_t gstride = (int64_t)gridDim.x * QZ_THREADS;
     uint32_t m = 0;
@@ -420,8 +445,9 @@ static int blocks_for(int64_t work)
 }
 
 // Publishes grid row y's tensor from the nblocks workgroup maxima of its
-// amax pass (current scaling: amax and the step) or of its measuring cast
-// (delayed scaling: amax and the measured step, or the ring update).
+// measuring cast (delayed scaling: amax and the measured step, or the ring
+// update).  Current scaling needs no such launch: its cast pass reduces the
+// amax pass's maxima itself.
 __global__ __launch_bounds__(1024) void qz_publish_parts(QzPack pk, int nblocks)
 {
     const QzParams &p = pk.t[blockIdx.y];
@@ -455,9 +481,8 @@ static hipError_t launch_tensor_pack(const QzPack &pk_in, int ntensors, hipStrea
         if (pk.t[0].amax_part)
             hipLaunchKernelGGL(qz_publish_parts, dim3(1, ntensors), dim3(1024), 0, s, pk, (int)grid.x);
     } else {
+        // With per-workgroup maxima the cast reduces them and publishes.
         hipLaunchKernelGGL((qz_amax<T, MODE>), grid, dim3(QZ_THREADS), 0, s, pk);
-        if (pk.t[0].amax_part)
-            hipLaunchKernelGGL(qz_publish_parts, dim3(1, ntensors), dim3(1024), 0, s, pk, (int)grid.x);
         hipLaunchKernelGGL((qz_cast<T, FMT, MODE, false>), grid, dim3(QZ_THREADS), 0, s, pk);
     }
     return hipGetLastError();
