@@ -478,10 +478,7 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         // K-major operands with at least one 256 x 256 tile per CU: the
         // pipelined direct-to-LDS kernel.
-        // The pipelined kernel covers FP8 only: INT8's paired 32-deep MFMAs do
-        // not fit its register budget.
-        if constexpr (AF != FMT_INT8)
-            if (p.fast && big >= 256 && p.batch <= 1 && p.K > 0) return launch_nt<AF, BF>(p, s);
+        if (p.fast && big >= 256 && p.batch <= 1 && p.K > 0) return launch_nt<AF, BF>(p, s);
         if (p.fast) {
             // The largest tile that still gives every CU a workgroup (batch
             // items count: they are grid rows).

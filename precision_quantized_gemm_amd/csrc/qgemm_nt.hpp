@@ -4,7 +4,7 @@
 //
 // One workgroup of 4 waves computes a 256 x 256 output tile; each wave owns
 // a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x64_f8f6f4 (FP8,
-// per-operand formats; INT8 takes the general kernel).
+// per-operand formats; INT8 as two v_mfma_i32_32x32x32_i8 per block).
 //
 // K advances 128 bytes per step -- whole 128-byte cache lines of every row
 // -- through 2 LDS stages of 64 KiB (256 rows of A and of B, 128 bytes per
@@ -93,6 +93,23 @@ template <int AF, int BF> struct Mma32 {
     __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return __float_as_uint(c[r]); }
 };
 
+// INT8: two v_mfma_i32_32x32x32_i8 per 64-deep fragment pair.  Each takes
+// 16 of a lane's 32 bytes (the low halves, then the high ones) from A and B
+// alike, so the two cover every k of the pair once; the sum does not depend
+// on which k each instruction sees.  The accumulator layout is the FP32
+// one's.
+template <> struct Mma32<FMT_INT8, FMT_INT8> {
+    typedef v16i acc_t;
+    static constexpr bool INT_ACC = true;
+    __device__ __forceinline__ static void run(acc_t &c, const u32x4 &a0, const u32x4 &a1, const u32x4 &b0,
+                                               const u32x4 &b1)
+    {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a0, (v4i)b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a1, (v4i)b1, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return (uint32_t)c[r]; }
+};
+
 
 // 32 rows x 64 k fragment for lane l: row (l & 31), k = 64*half +
 // 32*(l >> 5) .. +31 (logical chunks 4*half + 2*(l >> 5) and the next).
@@ -136,20 +153,29 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
 }
 
 
-// Fast-path epilogue of 16 consecutive FP32 accumulators of one row
-// (per-tensor scales, column a multiple of 16, output and bias rows 16-byte
-// aligned, all 16 inside the output): v = acc * sa * sb (+ bias), then one
-// to four 16-byte stores.  Returns the running max |v| as FP32 bits.
+// Fast-path epilogue of 16 consecutive accumulators of one row (per-tensor
+// scales or raw INT32 output, column a multiple of 16, output and bias rows
+// 16-byte aligned, all 16 inside the output): v = acc * sa * sb (+ bias),
+// then one to four 16-byte stores; INT32 output stores the accumulators.
+// Returns the running max |v| as FP32 bits.
+template <bool INT_ACC>
 __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilogue &epi, const uint4 (&w)[4],
                                                int64_t row, int64_t col, uint32_t vmax)
 {
+    if (INT_ACC && p.out_dt == DT_INT32) {
+        uint4 *out = reinterpret_cast<uint4 *>(static_cast<int32_t *>(p.out) + row * p.ldo + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = w[q];
+        return vmax;
+    }
+    auto val = [](uint32_t x) { return INT_ACC ? (float)(int32_t)x : __uint_as_float(x); };
     float v[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        v[4 * q + 0] = __uint_as_float(w[q].x) * epi.s_ab;
-        v[4 * q + 1] = __uint_as_float(w[q].y) * epi.s_ab;
-        v[4 * q + 2] = __uint_as_float(w[q].z) * epi.s_ab;
-        v[4 * q + 3] = __uint_as_float(w[q].w) * epi.s_ab;
+        v[4 * q + 0] = val(w[q].x) * epi.s_ab;
+        v[4 * q + 1] = val(w[q].y) * epi.s_ab;
+        v[4 * q + 2] = val(w[q].z) * epi.s_ab;
+        v[4 * q + 3] = val(w[q].w) * epi.s_ab;
     }
     if (p.bias_dt == DT_FP32) {
         const float4 *b = reinterpret_cast<const float4 *>(static_cast<const float *>(p.bias) + col);
@@ -213,7 +239,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
 {
     static_assert(!(CHAIN && KTAIL), "a chained grid needs whole k-steps");
     typedef Mma32<BF, AF> MMA;                 // operands swapped: acc holds C^T
-    static_assert(AF != FMT_INT8 && BF != FMT_INT8, "the pipelined kernel is FP8 only");
     constexpr int RPS = NT_READS_PER_SLOT;
     typedef typename MMA::acc_t acc_t;
     constexpr int WM = NT_BM / 2, WN = NT_BN / 2, TM = WM / 32, TN = WN / 32;
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         // LDS clock touch 16 distinct bank slots.
         const GemmParams &pe = p;
         const Epilogue epi(pe);
-        if (CHAIN || (epi.per_tensor && p.out_vec16 && p.bias_vec16 && whole)) {
+        if (CHAIN || ((epi.per_tensor || p.out_dt == DT_INT32) && p.out_vec16 && p.bias_vec16 && whole)) {
             // One block per iteration at run time (keeps the code and register
             // pressure small); the block's accumulators are picked out through
             // compile-time indices.
@@ -486,7 +511,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                                     make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
                 const int64_t row = m0 + wm0 + i * 32 + lr;
                 const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                vmax = nt_store16(pe, epi, w, row, col, vmax);
+                vmax = nt_store16<MMA::INT_ACC>(pe, epi, w, row, col, vmax);
             }
         } else if constexpr (!CHAIN) {
             constexpr int EP_LD = WN + 4;                    // padded row, in words
@@ -546,8 +571,9 @@ hipError_t launch_nt(GemmParams p, hipStream_t s)
     // steps; otherwise one tile per workgroup.
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     const int64_t cus = device_cu_count();
-    const bool chain = p.M % NT_BM == 0 && p.N % NT_BN == 0 && p.K % (2 * NT_BK) == 0 && p.sa_group == 0 &&
-                       p.sb_group == 0 && p.out_vec16 && p.bias_vec16 && tiles > cus;
+    const bool chain = p.M % NT_BM == 0 && p.N % NT_BN == 0 && p.K % (2 * NT_BK) == 0 &&
+                       ((p.sa_group == 0 && p.sb_group == 0) || p.out_dt == DT_INT32) && p.out_vec16 &&
+                       p.bias_vec16 && tiles > cus;
     const int64_t grid = chain ? cus : tiles;
     if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
     if (chain)

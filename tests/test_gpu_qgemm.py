@@ -469,3 +469,31 @@ def test_pipelined_chained_grid(orc, K, out_dtype, bias_kind, af, bf):
     else:
         print("chained grid", check_float(got, v, S, H, sasb, K, bias=bias_of(bias_vals, ns),
                                           what=f"chained {out_dtype}"))
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype,sag", [(8192, 5120, 512, "int32", 1), (8192, 5120, 256, "bf16", 0),
+                                                 (4096 + 37, 4096 + 48, 1024, "fp32", 1),
+                                                 (4096, 4096, 1040, "int32", 0)])
+def test_pipelined_int8(orc, M, N, K, out_dtype, sag):
+    """INT8 x INT8 on the pipelined kernel (two 32 x 32 x 32 integer MFMAs
+    per 64-deep fragment pair): the persistent grid with raw INT32 output
+    (any scale granularity) or per-tensor BF16 output, ragged tiles with
+    per-row FP32 output (the LDS epilogue), and a partial last k-step.
+    INT32 accumulators bit for bit, float outputs within the bound; sampled
+    entries include one in every 256 x 256 tile."""
+    a = finite_codes(orc, 81, 2, M, K, 2)
+    b = finite_codes(orc, 82, 2, N, K, 2)
+    rng = np.random.default_rng(83)
+    sa = (rng.random(M if sag else 1) * 0.01 + 0.001).astype(np.float32)
+    sb = (rng.random(N if sag else 1) * 0.01 + 0.001).astype(np.float32)
+    tm, tn = np.meshgrid(np.arange((M + 255) // 256), np.arange((N + 255) // 256), indexing="ij")
+    pm = np.minimum(tm.ravel() * 256 + rng.integers(0, 256, tm.size), M - 1).astype(np.int64)
+    pn = np.minimum(tn.ravel() * 256 + rng.integers(0, 256, tn.size), N - 1).astype(np.int64)
+    sm, sn = sampled_entries(M, N, rows=2, cols=2, rand=2000, seed=84)
+    ms, ns = np.concatenate([pm, sm, [M - 1]]), np.concatenate([pn, sn, [N - 1]])
+    acc, S, iacc, H, v, sasb = oracle_entries(orc, a, 2, 0, b, 2, 0, K, ms, ns, sa, sag, sb, sag, None)
+    out = run_gpu(a, 2, 0, b, 2, 0, K, sa, sag, sb, sag, out_dtype=out_dtype)
+    if out_dtype == "int32":
+        assert np.array_equal(out.numpy()[ms, ns].astype(np.int64), iacc)
+    else:
+        print("int8 pipelined", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, what=f"int8 {out_dtype}"))
