@@ -486,32 +486,36 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         const GemmParams &pe = p;
         const Epilogue epi(pe);
         if (CHAIN || ((epi.per_tensor || p.out_dt == DT_INT32) && p.out_vec16 && p.bias_vec16 && whole)) {
-            // One block per iteration at run time (keeps the code and register
-            // pressure small); the block's accumulators are picked out through
-            // compile-time indices.
+            // One row of blocks per iteration at run time, its 4 blocks
+            // unrolled (keeps the code and register pressure small); each
+            // block's accumulators are picked out through compile-time
+            // indices.
 #pragma unroll 1
-            for (int b = 0; b < TM * TN; ++b) {
-                const int i = b / TN, j = b % TN;
-                uint32_t x[16];
-                nt_unroll<0, TM * TN>([&](auto B) {
-                    constexpr int bb = decltype(B)::value;
-                    if (b == bb) {
+            for (int i = 0; i < TM; ++i) {
+                nt_unroll<0, TN>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    uint32_t x[16];
+                    nt_unroll<0, TM>([&](auto I) {
+                        constexpr int ii = decltype(I)::value;
+                        if (i == ii) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) x[r] = MMA::bits(acc[bb / TN][bb % TN], r);
+                            for (int r = 0; r < 16; ++r) x[r] = MMA::bits(acc[ii][j], r);
+                        }
+                    });
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const auto s02 = __builtin_amdgcn_permlane32_swap(x[r], x[8 + r], false, false);
+                        x[r] = s02[0]; x[8 + r] = s02[1];
+                        const auto s13 = __builtin_amdgcn_permlane32_swap(x[4 + r], x[12 + r], false, false);
+                        x[4 + r] = s13[0]; x[12 + r] = s13[1];
                     }
+                    const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
+                                        make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
+                    const int64_t row = m0 + wm0 + i * 32 + lr;
+                    const int64_t col = n0 + wn0 + j * 32 + h * 16;
+                    vmax = nt_store16<MMA::INT_ACC>(pe, epi, w, row, col, vmax);
+                    __builtin_amdgcn_sched_barrier(0);
                 });
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const auto s02 = __builtin_amdgcn_permlane32_swap(x[r], x[8 + r], false, false);
-                    x[r] = s02[0]; x[8 + r] = s02[1];
-                    const auto s13 = __builtin_amdgcn_permlane32_swap(x[4 + r], x[12 + r], false, false);
-                    x[4 + r] = s13[0]; x[12 + r] = s13[1];
-                }
-                const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
-                                    make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
-                const int64_t row = m0 + wm0 + i * 32 + lr;
-                const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                vmax = nt_store16<MMA::INT_ACC>(pe, epi, w, row, col, vmax);
             }
         } else if constexpr (!CHAIN) {
             constexpr int EP_LD = WN + 4;                    // padded row, in words
