@@ -202,3 +202,47 @@ def test_linear_forward_static(orc, M, N, K, fmt, bias_kind):
     got = r.out.cpu().to(torch.float64).numpy()[ms, ns]
     print("static", check_float(got, ref_v, ref["S"], ref["H"], float(ref["sx"][0]) * float(sw[0]), K,
                                 bias=bias_vals, what=f"static {M}x{N}x{K} fmt={fmt} bias={bias_kind}"))
+
+
+@pytest.mark.parametrize("M,N,K,fmt,bias_kind,out_dtype", [
+    (512, 128, 128, "e4m3", "fp32", "bf16"),     # the tiny workload's shape
+    (64, 32, 64, "e5m2", None, "fp32"),
+    (256, 96, 192, "e4m3", "bf16", "e4m3"),
+    (32, 512, 256, "e5m2", "fp32", "bf16"),
+    (768, 256, 128, "e4m3", None, "bf16"),
+    (800, 256, 128, "e4m3", "fp32", "bf16"),
+])
+def test_linear_forward_small_layers(orc, M, N, K, fmt, bias_kind, out_dtype):
+    """Small BF16 layers with current scaling to either FP8 format, every
+    bias kind and output type: codes, amax and steps bit for bit against the
+    oracle, outputs within the float bound (E4M3 outputs in the acceptance
+    set), out_amax equal to max |v| of the FP32 output of the same call."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    x = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32) * 3.0).to(torch.bfloat16)
+    w = torch.from_numpy(rng.standard_normal((N, K), dtype=np.float32) / np.sqrt(K)).to(torch.bfloat16)
+    b32 = (rng.standard_normal(N, dtype=np.float32) * 0.1).astype(np.float32)
+    bias = {"fp32": torch.from_numpy(b32), "bf16": torch.from_numpy(b32).to(torch.bfloat16), None: None}[bias_kind]
+    bias_vals = None if bias is None else bias.float().numpy()
+    f = {"e4m3": orc.E4M3, "e5m2": orc.E5M2}[fmt]
+    ref = orc.linear_forward(_bits(x), _bits(w), bias_vals, f)
+    r32 = q.linear_forward(x.cuda(), w.cuda(), None if bias is None else bias.cuda(), fmt, out_dtype="fp32",
+                           out_amax=True)
+    torch.cuda.synchronize()
+    _compare_quant(r32, ref)
+    assert r32.out_amax.item() == r32.out.abs().max().item()
+    os_ = np.float32(r32.out_amax.item() / 448.0) if out_dtype == "e4m3" else None
+    r = q.linear_forward(x.cuda(), w.cuda(), None if bias is None else bias.cuda(), fmt, out_dtype=out_dtype,
+                         out_scale=None if os_ is None else torch.tensor([os_], device="cuda"), out_amax=True)
+    torch.cuda.synchronize()
+    _compare_quant(r, ref)
+    assert r.out_amax.item() == r32.out_amax.item()
+    sasb = np.float64(ref["sx"][0]) * np.float64(ref["sw"][0])
+    bias_n = None if bias_vals is None else bias_vals.astype(np.float64)[ref["ns"]]
+    got = r.out.cpu()
+    if out_dtype == "e4m3":
+        differ = check_fp8_out(got.numpy()[ref["ms"], ref["ns"]], ref["v"], ref["S"], ref["H"], sasb, K, os_, orc,
+                               bias=bias_n, what="small e4m3")
+        print("small layer e4m3 differing codes:", differ)
+    else:
+        vals = got.to(torch.float64).numpy()[ref["ms"], ref["ns"]]
+        print("small layer", check_float(vals, ref["v"], ref["S"], ref["H"], sasb, K, bias=bias_n, what="small"))
