@@ -38,13 +38,14 @@
 // consecutive output columns of one row, which the epilogue moves through
 // LDS with 16-byte writes.
 //
-// The grid is persistent when K is a whole number of steps: one workgroup
-// per CU walks tiles id, id + grid, ...  When a tile's epilogue stays in registers (whole tile, per-tensor
-// scales, 16-byte aligned rows) and K is an even number of whole steps, the
-// two refills past its last step fetch the next tile's first two steps
-// instead of nothing, and the last step reads the next tile's first
-// fragments.  The next tile's start-up latency then hides behind this
-// tile's epilogue, and no workgroup launch separates the two.
+// The grid is persistent (CHAIN) when every tile is whole, every epilogue
+// stays in registers (per-tensor scales or raw INT32 output, 16-byte
+// aligned rows) and K is an even number of whole steps: one workgroup per
+// CU walks tiles id, id + grid, ...  The two refills past a tile's last
+// step fetch the next tile's first two steps instead of nothing, and the
+// last step reads the next tile's first fragments, so the next tile's
+// start-up latency hides behind this tile's epilogue and no workgroup
+// launch separates the two.  Other shapes take one tile per workgroup.
 #pragma once
 
 #include "qgemm_common.hpp"
