@@ -207,8 +207,18 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
             v[e] += (p.bias_dt == BIAS_Q_E4M3 ? fp8_decode<FMT_E4M3>(c) : fp8_decode<FMT_E5M2>(c)) * bs;
         }
     }
+    {
+        // max |v| as a float maximum with |.| source modifiers (three
+        // operands per instruction); for the finite values of the contract
+        // it is the maximum of the |v| bit patterns.
+        float m = __builtin_fabsf(v[0]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { const uint32_t b = absbits_f32(v[e]); vmax = b > vmax ? b : vmax; }
+        for (int e = 1; e < 16; e += 2)
+            m = __builtin_elementwise_maximum(
+                m, __builtin_elementwise_maximum(__builtin_fabsf(v[e]), e + 1 < 16 ? __builtin_fabsf(v[e + 1]) : 0.0f));
+        const uint32_t b = __float_as_uint(m);
+        vmax = b > vmax ? b : vmax;
+    }
     const int64_t o = row * p.ldo + col;
     if (p.out_dt == DT_E4M3) {
         const float s = epi.inv_os;
