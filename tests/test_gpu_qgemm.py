@@ -497,3 +497,32 @@ def test_pipelined_int8(orc, M, N, K, out_dtype, sag):
         assert np.array_equal(out.numpy()[ms, ns].astype(np.int64), iacc)
     else:
         print("int8 pipelined", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, what=f"int8 {out_dtype}"))
+
+
+@pytest.mark.parametrize("M,N", [(64, 96), (4096, 4096)])
+def test_int8_largest_k_extremes(orc, M, N):
+    """INT8 at the largest K the INT32 accumulator contract allows
+    (K * 127^2 <= 2^31 - 1: K = 133144, a partial last k-step), with every
+    product at +-127^2: the accumulators reach +-2,147,479,576 and must be
+    exact.  A rows are +127 (row 1: -127); B rows are +127 (row 2
+    alternates +127, -127, so its sums cancel): acc[m, n] = a_m * sum_k
+    b[n, k], checked everywhere, and sampled entries against the oracle.
+    (4096 x 4096 takes the pipelined kernel, 64 x 96 the general one.)  One
+    more k is rejected before anything runs."""
+    K = 133144
+    a = np.full((M, K), 127, dtype=np.int8)
+    a[1] = -127
+    b = np.full((N, K), 127, dtype=np.int8)
+    b[2, 1::2] = -127
+    out = run_gpu(a.view(np.uint8), 2, 0, b.view(np.uint8), 2, 0, K, [1.0], 0, [1.0], 0, out_dtype="int32").numpy()
+    bsum = b.astype(np.int64).sum(axis=1)
+    expect = np.where(np.arange(M)[:, None] == 1, -127, 127).astype(np.int64) * bsum[None, :]
+    assert expect[0, 0] == 127 * 127 * K == 2147479576
+    assert np.array_equal(out.astype(np.int64), expect)
+    ms = np.array([0, 1, 1, M - 1, 0], dtype=np.int64)
+    ns = np.array([0, 0, 2, N - 1, 2], dtype=np.int64)
+    _, _, iacc, _ = orc.qgemm_entries(a.view(np.uint8), 2, 0, b.view(np.uint8), 2, 0, K, ms, ns)
+    assert np.array_equal(out[ms, ns].astype(np.int64), iacc)
+    with pytest.raises(ValueError):
+        run_gpu(np.zeros((M, K + 1), np.uint8), 2, 0, np.zeros((N, K + 1), np.uint8), 2, 0, K + 1, [1.0], 0, [1.0], 0,
+                out_dtype="int32")
