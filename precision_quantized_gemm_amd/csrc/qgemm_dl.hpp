@@ -249,9 +249,11 @@ __global__ __launch_bounds__(GEMM_THREADS, MINW) void qgemm_dl_kernel(GemmParams
         // flight), then for every wave's: the barrier also means that every
         // wave is done with step kt-1, whose buffer the next refill takes.
         const int ahead = nk - 1 - kt < STAGES - 2 ? nk - 1 - kt : STAGES - 2;   // steps issued after kt
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * LOADS) & 0xF) | (((2 * LOADS) >> 4) << 14));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (LOADS & 0xF) | ((LOADS >> 4) << 14));
-        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        dl_unroll<0, STAGES - 1>([&](auto A) {
+            constexpr int n = decltype(A)::value * LOADS;   // vmcnt(ahead * LOADS)
+            static_assert(n < 64, "vmcnt holds 6 bits");
+            if (ahead == decltype(A)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 0xF) | ((n >> 4) << 14));
+        });
         // A bare barrier: a fenced one would also wait for the later steps'
         // loads.  Every wave's reads of step kt-1 are complete here (the
         // matrix cores consumed them).
