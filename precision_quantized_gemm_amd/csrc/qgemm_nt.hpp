@@ -159,11 +159,13 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
 // 16-byte aligned, all 16 inside the output): v = acc * sa * sb (+ bias),
 // then one to four 16-byte stores; INT32 output stores the accumulators.
 // Returns the running max |v| as FP32 bits.
-template <bool INT_ACC>
+// OD: the output dtype, fixed at compile time by the caller's dispatch;
+// HB: whether a bias is present (its kind is still tested at run time).
+template <bool INT_ACC, int OD, bool HB>
 __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilogue &epi, const uint4 (&w)[4],
                                                int64_t row, int64_t col, uint32_t vmax)
 {
-    if (INT_ACC && p.out_dt == DT_INT32) {
+    if constexpr (INT_ACC && OD == DT_INT32) {
         uint4 *out = reinterpret_cast<uint4 *>(static_cast<int32_t *>(p.out) + row * p.ldo + col);
 #pragma unroll
         for (int q = 0; q < 4; ++q) out[q] = w[q];
@@ -178,7 +180,8 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
         v[4 * q + 2] = val(w[q].z) * epi.s_ab;
         v[4 * q + 3] = val(w[q].w) * epi.s_ab;
     }
-    if (p.bias_dt == DT_FP32) {
+    if constexpr (!HB) {
+    } else if (p.bias_dt == DT_FP32) {
         const float4 *b = reinterpret_cast<const float4 *>(static_cast<const float *>(p.bias) + col);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -220,7 +223,7 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
         vmax = b > vmax ? b : vmax;
     }
     const int64_t o = row * p.ldo + col;
-    if (p.out_dt == DT_E4M3) {
+    if constexpr (OD == DT_E4M3) {
         const float s = epi.inv_os;
         uint4 c;
         c.x = encode4<FMT_E4M3>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
@@ -228,7 +231,7 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
         c.z = encode4<FMT_E4M3>(v[8] * s, v[9] * s, v[10] * s, v[11] * s);
         c.w = encode4<FMT_E4M3>(v[12] * s, v[13] * s, v[14] * s, v[15] * s);
         *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + o) = c;
-    } else if (p.out_dt == DT_BF16) {
+    } else if constexpr (OD == DT_BF16) {
         uint32_t hw[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -496,11 +499,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         // LDS clock touch 16 distinct bank slots.
         const GemmParams &pe = p;
         const Epilogue epi(pe);
-        if (CHAIN || ((epi.per_tensor || p.out_dt == DT_INT32) && p.out_vec16 && p.bias_vec16 && whole)) {
-            // One row of blocks per iteration at run time, its 4 blocks
-            // unrolled (keeps the code and register pressure small); each
-            // block's accumulators are picked out through compile-time
-            // indices.
+        // The register path, one row of blocks per iteration at run time,
+        // its 4 blocks unrolled (keeps the code and register pressure
+        // small); each block's accumulators are picked out through
+        // compile-time indices.  The output dtype and the presence of a
+        // bias are fixed per tile, so the blocks carry no tests for them.
+        auto regs_rows = [&](auto OD_, auto HB_) {
+            constexpr int OD = decltype(OD_)::value;
+            constexpr bool HB = decltype(HB_)::value;
 #pragma unroll 1
             for (int i = 0; i < TM; ++i) {
                 nt_unroll<0, TN>([&](auto J) {
@@ -524,9 +530,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                                         make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
                     const int64_t row = m0 + wm0 + i * 32 + lr;
                     const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                    vmax = nt_store16<MMA::INT_ACC>(pe, epi, w, row, col, vmax);
+                    vmax = nt_store16<MMA::INT_ACC, OD, HB>(pe, epi, w, row, col, vmax);
                     __builtin_amdgcn_sched_barrier(0);
                 });
+            }
+        };
+        typedef std::integral_constant<bool, true> HasBias;
+        typedef std::integral_constant<bool, false> NoBias;
+        if (CHAIN || ((epi.per_tensor || p.out_dt == DT_INT32) && p.out_vec16 && p.bias_vec16 && whole)) {
+            const bool hb = pe.bias_dt >= 0;
+            if (MMA::INT_ACC && pe.out_dt == DT_INT32) {
+                if constexpr (MMA::INT_ACC) regs_rows(std::integral_constant<int, DT_INT32>{}, NoBias{});
+            } else if (pe.out_dt == DT_E4M3) {
+                if (hb) regs_rows(std::integral_constant<int, DT_E4M3>{}, HasBias{});
+                else regs_rows(std::integral_constant<int, DT_E4M3>{}, NoBias{});
+            } else if (pe.out_dt == DT_BF16) {
+                if (hb) regs_rows(std::integral_constant<int, DT_BF16>{}, HasBias{});
+                else regs_rows(std::integral_constant<int, DT_BF16>{}, NoBias{});
+            } else {
+                if (hb) regs_rows(std::integral_constant<int, DT_FP32>{}, HasBias{});
+                else regs_rows(std::integral_constant<int, DT_FP32>{}, NoBias{});
             }
         } else if constexpr (!CHAIN) {
             constexpr int EP_LD = WN + 4;                    // padded row, in words
