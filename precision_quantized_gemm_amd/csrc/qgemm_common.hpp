@@ -33,17 +33,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // two multiplies is within the float acceptance bound).  E4M3 output
 // multiplies by RN(1/out_scale): its result differs from the correctly
 // rounded quotient by at most one FP32 rounding, which the FP8 acceptance
-// set allows for.
+// set allows for; with per-tensor scales and no bias the accumulator is
+// multiplied once by RN(sa*sb * RN(1/out_scale)) instead (the same number
+// of roundings).
 struct Epilogue {
     const GemmParams &p;
     float inv_os;       // RN(1 / out_scale) for E4M3 output
     float s_ab;         // sa[0] * sb[0] when both are per tensor
+    float s_out;        // RN(s_ab * inv_os): E4M3 output, per-tensor scales, no bias
     bool per_tensor;
     __device__ __forceinline__ explicit Epilogue(const GemmParams &pp) : p(pp)
     {
         inv_os = pp.out_dt == DT_E4M3 ? 1.0f / pp.out_scale[0] : 1.0f;
         per_tensor = pp.sa_group == 0 && pp.sb_group == 0;
         s_ab = (per_tensor && pp.out_dt != DT_INT32) ? pp.sa[0] * pp.sb[0] : 1.0f;
+        s_out = s_ab * inv_os;
     }
 
     __device__ __forceinline__ float bias_at(int64_t col) const
@@ -107,7 +111,15 @@ struct Epilogue {
             if (n == 4 && p.out_vec4) *reinterpret_cast<float4 *>(out) = make_float4(v[0], v[1], v[2], v[3]);
             else for (int e = 0; e < n; ++e) out[e] = v[e];
         } else {
-            const uint32_t c = encode4<FMT_E4M3>(v[0] * inv_os, v[1] * inv_os, v[2] * inv_os, v[3] * inv_os);
+            // Per-tensor scales and no bias: one multiply of the accumulator
+            // by RN(sa*sb / out_scale); otherwise v times RN(1 / out_scale).
+            float u[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                u[e] = (per_tensor && p.bias_dt < 0)
+                           ? (INT_ACC ? (float)(int32_t)raw[e] : __uint_as_float(raw[e])) * s_out
+                           : v[e] * inv_os;
+            const uint32_t c = encode4<FMT_E4M3>(u[0], u[1], u[2], u[3]);
             uint8_t *out = static_cast<uint8_t *>(p.out) + o;
             if (n == 4 && p.out_vec4) *reinterpret_cast<uint32_t *>(out) = c;
             else for (int e = 0; e < n; ++e) out[e] = (uint8_t)(c >> (8 * e));

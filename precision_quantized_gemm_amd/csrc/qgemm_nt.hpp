@@ -163,8 +163,34 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
 // HB: whether a bias is present (its kind is still tested at run time).
 template <bool INT_ACC, int OD, bool HB>
 __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilogue &epi, const uint4 (&w)[4],
-                                               int64_t row, int64_t col, uint32_t vmax)
+                                               int64_t row, int64_t col, uint32_t vmax, float &macc)
 {
+    if constexpr (OD == DT_E4M3 && !HB) {
+        // No bias: the codes are the accumulators times RN(sa*sb /
+        // out_scale), and out_amax is max |acc| times |sa*sb| once per
+        // workgroup (rounding is monotone, so that is max |RN(acc*sa*sb)|);
+        // this keeps max |acc| in macc.
+        auto val = [](uint32_t x) { return INT_ACC ? (float)(int32_t)x : __uint_as_float(x); };
+        float a[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            a[4 * q + 0] = val(w[q].x); a[4 * q + 1] = val(w[q].y);
+            a[4 * q + 2] = val(w[q].z); a[4 * q + 3] = val(w[q].w);
+        }
+        float m = macc;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2)
+            m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_fabsf(a[e]), __builtin_fabsf(a[e + 1])));
+        macc = m;
+        const float s = epi.s_out;
+        uint4 c;
+        c.x = encode4<FMT_E4M3>(a[0] * s, a[1] * s, a[2] * s, a[3] * s);
+        c.y = encode4<FMT_E4M3>(a[4] * s, a[5] * s, a[6] * s, a[7] * s);
+        c.z = encode4<FMT_E4M3>(a[8] * s, a[9] * s, a[10] * s, a[11] * s);
+        c.w = encode4<FMT_E4M3>(a[12] * s, a[13] * s, a[14] * s, a[15] * s);
+        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + row * p.ldo + col) = c;
+        return vmax;
+    }
     if constexpr (INT_ACC && OD == DT_INT32) {
         uint4 *out = reinterpret_cast<uint4 *>(static_cast<int32_t *>(p.out) + row * p.ldo + col);
 #pragma unroll
@@ -507,6 +533,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         auto regs_rows = [&](auto OD_, auto HB_) {
             constexpr int OD = decltype(OD_)::value;
             constexpr bool HB = decltype(HB_)::value;
+            float macc = 0.0f;   // max |acc| (E4M3 output without bias)
 #pragma unroll 1
             for (int i = 0; i < TM; ++i) {
                 nt_unroll<0, TN>([&](auto J) {
@@ -530,9 +557,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                                         make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
                     const int64_t row = m0 + wm0 + i * 32 + lr;
                     const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                    vmax = nt_store16<MMA::INT_ACC, OD, HB>(pe, epi, w, row, col, vmax);
+                    vmax = nt_store16<MMA::INT_ACC, OD, HB>(pe, epi, w, row, col, vmax, macc);
                     __builtin_amdgcn_sched_barrier(0);
                 });
+            }
+            if constexpr (OD == DT_E4M3 && !HB) {
+                const uint32_t b = __float_as_uint(macc * __builtin_fabsf(epi.s_ab));
+                vmax = b > vmax ? b : vmax;
             }
         };
         typedef std::integral_constant<bool, true> HasBias;
