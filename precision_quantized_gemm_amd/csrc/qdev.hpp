@@ -74,6 +74,12 @@ struct Divider {
     {
         return fast ? qdiv_fast(x, s, inv) : x / s;
     }
+    // The same with the path chosen at compile time (the caller tests
+    // `fast` once for a whole loop).
+    template <bool FAST> __device__ __forceinline__ float q(float x) const
+    {
+        return FAST ? qdiv_fast(x, s, inv) : x / s;
+    }
 };
 
 // ---------------------------------------------------------------------------

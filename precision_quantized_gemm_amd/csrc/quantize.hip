@@ -108,6 +108,18 @@ __device__ __forceinline__ uint4 encode16(const Vec16<T> &u, const Divider &div)
     return o;
 }
 
+// The same with the quotient path fixed at compile time.
+template <int FMT, bool FAST, typename T>
+__device__ __forceinline__ uint4 encode16q(const Vec16<T> &u, const Divider &d)
+{
+    uint4 o;
+    o.x = encode4<FMT>(d.q<FAST>(u.f(0)), d.q<FAST>(u.f(1)), d.q<FAST>(u.f(2)), d.q<FAST>(u.f(3)));
+    o.y = encode4<FMT>(d.q<FAST>(u.f(4)), d.q<FAST>(u.f(5)), d.q<FAST>(u.f(6)), d.q<FAST>(u.f(7)));
+    o.z = encode4<FMT>(d.q<FAST>(u.f(8)), d.q<FAST>(u.f(9)), d.q<FAST>(u.f(10)), d.q<FAST>(u.f(11)));
+    o.w = encode4<FMT>(d.q<FAST>(u.f(12)), d.q<FAST>(u.f(13)), d.q<FAST>(u.f(14)), d.q<FAST>(u.f(15)));
+    return o;
+}
+
 // Offsets of vector unit u in x and x_q for the two vector modes.
 template <int MODE>
 __device__ __forceinline__ void unit_offsets(const QzParams &p, int64_t u, int64_t &ox, int64_t &oq)
@@ -257,30 +269,37 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzPack pk)
     } else {
         // Unit u of the walk is unit n_units-1-u of the tensor in pass 2.
         auto phys = [&](int64_t u) { return MEASURE ? u : p.n_units - 1 - u; };
-        int64_t u = gtid;
-        for (; u + (QZ_UNROLL - 1) * gstride < p.n_units; u += QZ_UNROLL * gstride) {
-            Vec16<T> v[QZ_UNROLL];
-            int64_t oq[QZ_UNROLL];
+        // The quotient path is chosen once for the whole walk, so no element
+        // carries a test for it.
+        auto walk = [&](auto FASTC) {
+            constexpr bool FAST = decltype(FASTC)::value;
+            int64_t u = gtid;
+            for (; u + (QZ_UNROLL - 1) * gstride < p.n_units; u += QZ_UNROLL * gstride) {
+                Vec16<T> v[QZ_UNROLL];
+                int64_t oq[QZ_UNROLL];
 #pragma unroll
-            for (int j = 0; j < QZ_UNROLL; ++j) {
-                int64_t ox;
-                unit_offsets<MODE>(p, phys(u + j * gstride), ox, oq[j]);
-                v[j].load(x + ox);
-            }
+                for (int j = 0; j < QZ_UNROLL; ++j) {
+                    int64_t ox;
+                    unit_offsets<MODE>(p, phys(u + j * gstride), ox, oq[j]);
+                    v[j].load(x + ox);
+                }
 #pragma unroll
-            for (int j = 0; j < QZ_UNROLL; ++j) {
-                if (MEASURE) { uint32_t t = v[j].amax_bits(); m = t > m ? t : m; }
-                *reinterpret_cast<uint4 *>(xq + oq[j]) = encode16<FMT>(v[j], div);
+                for (int j = 0; j < QZ_UNROLL; ++j) {
+                    if (MEASURE) { uint32_t t = v[j].amax_bits(); m = t > m ? t : m; }
+                    *reinterpret_cast<uint4 *>(xq + oq[j]) = encode16q<FMT, FAST>(v[j], div);
+                }
             }
-        }
-        for (; u < p.n_units; u += gstride) {
-            int64_t ox, oq;
-            unit_offsets<MODE>(p, phys(u), ox, oq);
-            Vec16<T> v;
-            v.load(x + ox);
-            if (MEASURE) { uint32_t t = v.amax_bits(); m = t > m ? t : m; }
-            *reinterpret_cast<uint4 *>(xq + oq) = encode16<FMT>(v, div);
-        }
+            for (; u < p.n_units; u += gstride) {
+                int64_t ox, oq;
+                unit_offsets<MODE>(p, phys(u), ox, oq);
+                Vec16<T> v;
+                v.load(x + ox);
+                if (MEASURE) { uint32_t t = v.amax_bits(); m = t > m ? t : m; }
+                *reinterpret_cast<uint4 *>(xq + oq) = encode16q<FMT, FAST>(v, div);
+            }
+        };
+        if (div.fast) walk(std::true_type{});
+        else walk(std::false_type{});
         if (MODE == MODE_FLAT)
             for (int64_t e = p.n_units * QZ_UNIT + gtid; e < p.n_elems; e += gstride) {
                 float v = load1<T>(x, e);
