@@ -397,35 +397,41 @@ __global__ __launch_bounds__(QZ_ROW_THREADS) void qz_rows(QzParams p)
         if (p.scale_out) p.scale_out[grp] = step;
     }
     const Divider div(DELAYED ? p.scale_src[grp] : step);
-    for (int64_t r = r0 + tr, u = tu; r < r1 && u < W;) {
-        int64_t rr[QZ_UNROLL], uu[QZ_UNROLL];
-        bool ok[QZ_UNROLL];
+    // The quotient path is chosen once for the group's walk.
+    auto walk = [&](auto FASTC) {
+        constexpr bool FAST = decltype(FASTC)::value;
+        for (int64_t r = r0 + tr, u = tu; r < r1 && u < W;) {
+            int64_t rr[QZ_UNROLL], uu[QZ_UNROLL];
+            bool ok[QZ_UNROLL];
 #pragma unroll
-        for (int k = 0; k < QZ_UNROLL; ++k) {
-            ok[k] = r < r1;
-            rr[k] = r; uu[k] = u;
-            if (ok[k]) next(r, u);
+            for (int k = 0; k < QZ_UNROLL; ++k) {
+                ok[k] = r < r1;
+                rr[k] = r; uu[k] = u;
+                if (ok[k]) next(r, u);
+            }
+            if (VEC) {
+                Vec16<T> v[QZ_UNROLL];
+#pragma unroll
+                for (int k = 0; k < QZ_UNROLL; ++k)
+                    if (ok[k]) v[k].load(static_cast<const T *>(p.x) + rr[k] * p.ldx + uu[k] * QZ_UNIT);
+#pragma unroll
+                for (int k = 0; k < QZ_UNROLL; ++k)
+                    if (ok[k])
+                        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.xq) + rr[k] * p.ldq + uu[k] * QZ_UNIT) =
+                            encode16q<FMT, FAST>(v[k], div);
+            } else {
+                float v[QZ_UNROLL];
+#pragma unroll
+                for (int k = 0; k < QZ_UNROLL; ++k)
+                    v[k] = ok[k] ? load1<T>(static_cast<const T *>(p.x) + rr[k] * p.ldx, uu[k]) : 0.0f;
+#pragma unroll
+                for (int k = 0; k < QZ_UNROLL; ++k)
+                    if (ok[k]) static_cast<uint8_t *>(p.xq)[rr[k] * p.ldq + uu[k]] = encode1<FMT>(div.q<FAST>(v[k]));
+            }
         }
-        if (VEC) {
-            Vec16<T> v[QZ_UNROLL];
-#pragma unroll
-            for (int k = 0; k < QZ_UNROLL; ++k)
-                if (ok[k]) v[k].load(static_cast<const T *>(p.x) + rr[k] * p.ldx + uu[k] * QZ_UNIT);
-#pragma unroll
-            for (int k = 0; k < QZ_UNROLL; ++k)
-                if (ok[k])
-                    *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.xq) + rr[k] * p.ldq + uu[k] * QZ_UNIT) =
-                        encode16<FMT>(v[k], div);
-        } else {
-            float v[QZ_UNROLL];
-#pragma unroll
-            for (int k = 0; k < QZ_UNROLL; ++k)
-                v[k] = ok[k] ? load1<T>(static_cast<const T *>(p.x) + rr[k] * p.ldx, uu[k]) : 0.0f;
-#pragma unroll
-            for (int k = 0; k < QZ_UNROLL; ++k)
-                if (ok[k]) static_cast<uint8_t *>(p.xq)[rr[k] * p.ldq + uu[k]] = encode1<FMT>(div(v[k]));
-        }
-    }
+    };
+    if (div.fast) walk(std::true_type{});
+    else walk(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
