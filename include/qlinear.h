@@ -50,7 +50,7 @@ typedef enum {
     QL_ERR_DTYPE = 2,        /* unsupported dtype / format combination      */
     QL_ERR_SHAPE = 3,        /* leading dimension smaller than the row      */
     QL_ERR_NULL = 4,         /* a required pointer is NULL                  */
-    QL_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement */
+    QL_ERR_UNSUPPORTED = 5,  /* valid request the library does not implement */
     QL_ERR_HIP = 6           /* a HIP runtime call failed                   */
 } ql_status;
 
