@@ -55,12 +55,22 @@ def build(force: bool = True) -> Path:
     return _LIB
 
 
+def is_stale() -> bool:
+    """True when the library is missing or older than its C source."""
+    return not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime
+
+
 def _load():
+    """Load the built library.  Never compiles: a process that may already
+    have initialised the GPU must not start a compiler, so a missing or
+    stale library is an error here and only ``build()`` (called by the
+    package build and at the start of a test session) compiles."""
     global _lib
     if _lib is not None:
         return _lib
-    if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
-        build()
+    if is_stale():
+        raise ImportError(f"{_LIB} is missing or older than {_SRC.name}: run oracle.build() first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(str(_LIB))
     i64, i32, dbl, flt, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
     lib.orc_fp8_encode.argtypes = [dbl, i32]

@@ -246,3 +246,25 @@ def test_linear_forward_small_layers(orc, M, N, K, fmt, bias_kind, out_dtype):
     else:
         vals = got.to(torch.float64).numpy()[ref["ms"], ref["ns"]]
         print("small layer", check_float(vals, ref["v"], ref["S"], ref["H"], sasb, K, bias=bias_n, what="small"))
+
+
+def test_linear_forward_static_handworked(orc):
+    """The hand-worked static-inference case (tests/golden/static_handworked.txt)
+    through the C ABI: E5M2 layer, delayed step for x, pre-quantized weight
+    and bias.  Every intermediate is exact, so the FP32 output must equal
+    the fixture bit for bit, as must x's codes, the fresh step and amax."""
+    from conftest import read_golden
+    g = {r[0]: r[1:] for r in read_golden("static_handworked.txt")}
+    dev = "cuda"
+    x = torch.tensor([float(v) for v in g["x"]], dtype=torch.float32).reshape(2, 2).to(torch.bfloat16)
+    w_q = torch.tensor([int(c, 16) for c in g["w_codes"]], dtype=torch.uint8).reshape(2, 2)
+    b_q = torch.tensor([int(c, 16) for c in g["bias_codes"]], dtype=torch.uint8)
+    f1 = lambda v: torch.tensor([float(v)], dtype=torch.float32, device=dev)
+    r = q.linear_forward_static(x.to(dev), w_q.to(dev), f1(g["sw"][0]), bias=b_q.to(dev),
+                                bias_scale=f1(g["bias_scale"][0]), fmt="e5m2", sx_in=f1(g["sx_in"][0]),
+                                out_dtype="fp32")
+    torch.cuda.synchronize()
+    assert r.x_q.cpu().numpy().ravel().tolist() == [int(c, 16) for c in g["x_codes"]]
+    assert r.amax_x.item() == float(g["amax_x"][0])
+    assert r.sx.cpu().numpy()[0] == np.float32(3) / np.float32(57344)
+    assert r.out.cpu().numpy().ravel().tolist() == [float(v) for v in g["v"]]

@@ -262,24 +262,58 @@ def test_out_amax_and_fp8_output(orc):
     print("fp8 out", rep)
 
 
+def oracle_entries_threaded(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, sa, sb):
+    """oracle_entries for per-tensor scales and no bias, with the entries
+    split over the host's cores (each chunk is one oracle call; ctypes
+    releases the interpreter lock while it runs)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    n = max(1, min(16, os.cpu_count() or 1))
+    parts = np.array_split(np.arange(ms.size), n * 4)
+    with ThreadPoolExecutor(n) as pool:
+        res = list(pool.map(lambda i: orc.qgemm_entries(a_st, af, al, b_st, bf, bl, K, ms[i], ns[i]), parts))
+    acc, S, iacc, H = (np.concatenate([r[j] for r in res]) for j in range(4))
+    v = orc.epilogue(acc, ms, ns, np.asarray(sa, np.float32), 0, np.asarray(sb, np.float32), 0, None)
+    sasb = np.float64(np.float32(sa[0])) * np.float64(np.float32(sb[0]))
+    return acc, S, iacc, H, v, sasb
+
+
+def per_tile_entries(M, N, tile, seed):
+    """One random entry inside every tile x tile block of the output."""
+    rng = np.random.default_rng(seed)
+    tm, tn = np.meshgrid(np.arange(0, M, tile), np.arange(0, N, tile), indexing="ij")
+    tm, tn = tm.ravel(), tn.ravel()
+    ms = tm + rng.integers(0, tile, tm.size)
+    ns = tn + rng.integers(0, tile, tn.size)
+    return np.minimum(ms, M - 1).astype(np.int64), np.minimum(ns, N - 1).astype(np.int64)
+
+
 def test_large_fp8_sampled(orc):
-    """The large FP8 workload at full size (16384 x 8192 x 8192, E4M3 output
-    with out_scale = amax_prev/448) on sampled outputs: 4 full rows, 4 full
-    columns, 4096 random entries.  amax_prev is the oracle's max |v| over the
-    sampled rows (a previous measurement of the same product)."""
+    """The large FP8 workload at full size (16384 x 8192 x 8192) on the
+    launch configuration the benchmark times (persistent grid, register
+    epilogue), on sampled outputs: 8 full rows, 8 full columns, 4096 random
+    entries and one entry in every 256 x 256 tile.  E4M3 output with
+    out_scale = amax_prev/448 must lie in the acceptance set; a BF16-output
+    run of the same product gives the float bound's report (fraction of
+    entries within the stated bound alone).  amax_prev is the oracle's max
+    |v| over the sampled rows (a previous measurement of the same product)."""
     d = synth.workload("large_fp8")
     aq, sa, _ = orc.quantize(synth.bf16_bits(d["a"]), 0, 0)
     bq, sb, _ = orc.quantize(synth.bf16_bits(d["b"]), 0, 0)
     M, K = aq.shape
     N = bq.shape[0]
-    ms, ns = sampled_entries(M, N, rows=4, cols=4, rand=4096, seed=6)
-    acc, S, _, H, v, sasb = oracle_entries(orc, aq, 0, 0, bq, 0, 0, K, ms, ns, sa, 0, sb, 0, None)
-    amax_prev = np.abs(v[: 4 * N]).max()
+    ms, ns = sampled_entries(M, N, rows=8, cols=8, rand=4096, seed=6)
+    tms, tns = per_tile_entries(M, N, 256, seed=7)
+    ms, ns = np.concatenate([ms, tms]), np.concatenate([ns, tns])
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, aq, 0, 0, bq, 0, 0, K, ms, ns, sa, sb)
+    amax_prev = np.abs(v[: 8 * N]).max()
     os_ = np.float32(amax_prev / 448.0)
     out = run_gpu(aq, 0, 0, bq, 0, 0, K, sa, 0, sb, 0, out_dtype="e4m3", out_scale=os_)
     got = out.numpy()[ms, ns]
-    differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, what="large_fp8")
+    differ = check_fp8_out(got, v, S, H, sasb, K, os_, orc, what="large_fp8 e4m3")
     print("large_fp8 differing codes:", differ, "of", got.size)
+    out_b = run_gpu(aq, 0, 0, bq, 0, 0, K, sa, 0, sb, 0, out_dtype="bf16")
+    print("large_fp8 bf16", check_float(out_values(out_b)[ms, ns], v, S, H, sasb, K, what="large_fp8 bf16"))
 
 
 @pytest.mark.parametrize("af,bf,K", [(0, 0, 1040), (1, 0, 1040), (2, 2, 1040), (0, 0, 1152), (0, 1, 128),
@@ -526,3 +560,37 @@ def test_int8_largest_k_extremes(orc, M, N):
     with pytest.raises(ValueError):
         run_gpu(np.zeros((M, K + 1), np.uint8), 2, 0, np.zeros((N, K + 1), np.uint8), 2, 0, K + 1, [1.0], 0, [1.0], 0,
                 out_dtype="int32")
+
+
+def test_matrix_core_truncation_needs_H(orc):
+    """Why the float bound carries the oracle's H term.  Each output below
+    is a hand-built K = 16 dot product (E5M2, FP32 output, unit scales)
+    whose first group of 8 products holds +1 and -1 (exponent sum 0) and
+    six products of +-2^-14.  Exactly, the dot product is the six small
+    products; the matrix cores align the group to its largest exponent sum
+    and drop what lies below 2^-13 of it.  So the GPU result is outside the
+    stated bound (1 BF16 ulp + 1e-6 * sum |a_q b_q|) and inside H (one grid
+    step 2^(0-13) per product off that grid).  Row 3 puts the small
+    products in a group of their own: on its own grid nothing is dropped,
+    and the result is exact."""
+    one, tiny, neg_one, neg_tiny = 0x3C, 0x04, 0xBC, 0x84
+    K = 16
+    a = np.zeros((4, K), np.uint8)
+    a[0, :8] = [one, neg_one] + [tiny] * 6                 # exact 6 * 2^-14
+    a[1, :8] = [one, neg_one] + [neg_tiny] * 6             # exact -6 * 2^-14
+    a[2, :8] = [one, neg_one] + [tiny, neg_tiny, tiny, tiny, tiny, neg_tiny]   # exact 2 * 2^-14
+    a[3, :2] = [one, neg_one]
+    a[3, 8:14] = tiny                                      # second group: exact 6 * 2^-14
+    b = np.full((1, K), one, np.uint8)
+    ms, ns = all_entries(4, 1)
+    acc, S, _, H = orc.qgemm_entries(a, 1, 0, b, 1, 0, K, ms, ns)
+    assert acc.tolist() == [6 * 2.0 ** -14, -6 * 2.0 ** -14, 2 * 2.0 ** -14, 6 * 2.0 ** -14]
+    assert H.tolist() == [6 * 2.0 ** -13] * 3 + [0.0]
+    got = out_values(run_gpu(a, 1, 0, b, 1, 0, K, [1.0], 0, [1.0], 0, out_dtype="fp32")).ravel()
+    err = np.abs(got - acc)
+    from tolerance import float_bound, strict_bound
+    strict = strict_bound(acc, S, 1.0)
+    print("truncation probe: gpu", got.tolist(), "exact", acc.tolist(), "err/strict", (err / strict).tolist())
+    assert np.all(err[:3] > strict[:3]), "the matrix cores kept the small products: H would not be needed"
+    assert np.all(err <= float_bound(acc, S, H, 1.0, K))
+    assert got[3] == acc[3]

@@ -226,3 +226,45 @@ def test_batched_handworked(orc):
     acc, S, H, v = orc.qgemm_batched_entries(a, orc.E4M3, b, orc.E4M3, zs, ms, ns, sa, 1, sb, 2)
     assert list(acc) == [float(x) for x in g["batch_acc"]]
     assert list(v) == [float(x) for x in g["batch_v"]]
+
+
+def test_batched_bias_handworked(orc):
+    """The batched product's bias branch: an FP32 and a BF16 bias over the
+    output columns (tests/golden/groups_handworked.txt).  A bias indexed by
+    the row, read as float16, or added before the scales fails here."""
+    g = {r[0]: r[1:] for r in read_golden("groups_handworked.txt")}
+    a = np.array([int(c, 16) for c in g["batch_a"]], np.uint8).reshape(2, 1, 2)
+    b = np.array([int(c, 16) for c in g["batch_b"]], np.uint8).reshape(2, 2, 2)
+    zs, ms, ns = np.array([0, 0, 1, 1]), np.array([0, 0, 0, 0]), np.array([0, 1, 0, 1])
+    sa = [float(v) for v in g["batch_sa"]]
+    sb = [float(v) for v in g["batch_sb"]]
+    want = [float(x) for x in g["batch_v_bias"]]
+    bias32 = np.array([float(v) for v in g["batch_bias_f32"]], np.float32)
+    _, _, _, v32 = orc.qgemm_batched_entries(a, orc.E4M3, b, orc.E4M3, zs, ms, ns, sa, 1, sb, 2, bias=bias32)
+    assert list(v32) == want
+    bias16 = np.array([int(v, 16) for v in g["batch_bias_bf16"]], np.uint16)
+    _, _, _, v16 = orc.qgemm_batched_entries(a, orc.E4M3, b, orc.E4M3, zs, ms, ns, sa, 1, sb, 2, bias=bias16)
+    assert list(v16) == want
+
+
+def test_linear_forward_static_handworked(orc):
+    """Static FP8 inference (tests/golden/static_handworked.txt): x quantized
+    with a delayed step, a pre-quantized E5M2 weight with its step, and an
+    E5M2-coded bias times bias_scale.  A bias decoded in another format, a
+    dropped bias_scale or the fresh step used in place of the delayed one
+    each change the result."""
+    g = {r[0]: r[1:] for r in read_golden("static_handworked.txt")}
+    x = np.array([float(v) for v in g["x"]], np.float32).reshape(2, 2)
+    xb = synth.bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+    wq = np.array([int(c, 16) for c in g["w_codes"]], np.uint8).reshape(2, 2)
+    bq = np.array([int(c, 16) for c in g["bias_codes"]], np.uint8)
+    sx_in = np.array([float(g["sx_in"][0])], np.float32)
+    r = orc.linear_forward_static(xb, wq, orc.E5M2, np.array([float(g["sw"][0])], np.float32), bq,
+                                  float(g["bias_scale"][0]), orc.E5M2, sx_in=sx_in)
+    assert list(r["x_q"].ravel()) == [int(c, 16) for c in g["x_codes"]]
+    assert r["amax_x"][0] == float(g["amax_x"][0])
+    assert r["sx"][0] == np.float32(3) / np.float32(57344)     # the fresh step is still reported
+    assert r["sx_used"][0] == sx_in[0]
+    assert list(r["acc"]) == [float(v) for v in g["acc"]]
+    assert list(r["v"]) == [float(v) for v in g["v"]]
+    assert not r["H"].any()
