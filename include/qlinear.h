@@ -22,7 +22,9 @@
  *   All device work is enqueued on it; no call synchronizes the host and no
  *   call allocates device memory.
  * - The caller owns every buffer, including the workspace.  The library
- *   keeps no global mutable state besides a thread-local error string.
+ *   keeps no global mutable state besides a thread-local error string and,
+ *   for ql_linear_forward_noalloc only, that call's device scratch array
+ *   and the cache of its per-device address.
  * - Scales are quantization STEPS: codes are x / scale ([FP8PY] module
  *   docstring).  The library forms any reciprocal itself.  amax values are
  *   outputs only, never accumulated into, so callers never clear them.
@@ -239,6 +241,32 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                             void *x_q, float *sx, float *amax_x,
                             void *w_q, float *sw, float *amax_w,
                             void *ws, void *stream);
+
+/* ------------------------------------------------------------------------
+ * ql_linear_forward_noalloc -- ql_linear_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs and errors as ql_linear_forward, without `ws`: the
+ * workspace is a 1,311,744-byte array inside the library, one copy per
+ * GPU, held until the process ends.  Its size does not depend on M, N or
+ * K, so every size ql_linear_forward accepts is accepted.  The call makes
+ * no device allocation of any kind.  After validation it clears the
+ * array's election counters with a small fill kernel on `stream`, then
+ * enqueues the same kernels as ql_linear_forward.
+ *
+ * `stream` (NULL: the default stream) must belong to the current device;
+ * otherwise QL_ERR_VALUE.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams without ordering
+ * between them) race on it and give undefined results.
+ * ---------------------------------------------------------------------- */
+ql_status ql_linear_forward_noalloc(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
+                                    const void *w, int64_t N,
+                                    const void *bias, ql_dtype bias_dt, ql_qfmt fmt,
+                                    const float *sx_in, const float *sw_in,
+                                    void *out, ql_dtype out_dt, const float *out_scale, float *out_amax,
+                                    void *x_q, float *sx, float *amax_x,
+                                    void *w_q, float *sw, float *amax_w, void *stream);
 
 /* ------------------------------------------------------------------------
  * ql_quantize_groups -- one scale per group of rows.

@@ -11,7 +11,7 @@ precision_quantized_gemm_amd.build``).
 """
 from ._lib import (QL_DT_BF16, QL_DT_E4M3, QL_DT_FP32, QL_DT_INT32, QL_FMT_E4M3, QL_FMT_E5M2,
                    QL_FMT_INT8, QL_K_MAJOR, QL_MN_MAJOR, QL_PER_ROW, QL_PER_TENSOR, QLError,
-                   ql_last_error, ql_linear_backward, ql_linear_forward, ql_linear_forward_static, ql_qgemm, ql_qgemm_batched, ql_quantize,
+                   ql_last_error, ql_linear_backward, ql_linear_forward, ql_linear_forward_noalloc, ql_linear_forward_static, ql_qgemm, ql_qgemm_batched, ql_quantize,
                    ql_quantize_groups, ql_quantize_ring, ql_status_string,
                    ql_workspace_bytes, ql_workspace_init)
 from .api import (LinearGrads, LinearOut, linear_backward, linear_forward, linear_forward_static, new_workspace, qgemm,
@@ -19,6 +19,7 @@ from .api import (LinearGrads, LinearOut, linear_backward, linear_forward, linea
 
 __all__ = [
     "ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring", "ql_qgemm", "ql_linear_forward",
+    "ql_linear_forward_noalloc",
     "ql_linear_backward", "linear_backward", "LinearGrads", "ql_linear_forward_static", "linear_forward_static",
     "ql_quantize_groups", "ql_qgemm_batched", "quantize_groups", "qgemm_batched",
     "ql_status_string", "ql_last_error", "QLError",

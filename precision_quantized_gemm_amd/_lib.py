@@ -59,6 +59,9 @@ def load():
     lib.ql_linear_forward.argtypes = [vp, i32, i64, i64, vp, i64, vp, i32, i32, vp, vp,
                                       vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_forward.restype = i32
+    lib.ql_linear_forward_noalloc.argtypes = [vp, i32, i64, i64, vp, i64, vp, i32, i32, vp, vp,
+                                              vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ql_linear_forward_noalloc.restype = i32
     lib.ql_quantize_groups.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i64, vp, vp, vp]
     lib.ql_quantize_groups.restype = i32
     lib.ql_qgemm_batched.argtypes = [vp, i32, i32, i64, i64, vp, i32, i32, i64, i64, i64, i64, i64, i64,
@@ -122,6 +125,13 @@ def ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out
     _check(load().ql_linear_forward(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out,
                                     out_dt, out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w,
                                     ws, stream), "ql_linear_forward")
+
+
+def ql_linear_forward_noalloc(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out, out_dt,
+                              out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w, stream=0) -> None:
+    _check(load().ql_linear_forward_noalloc(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out,
+                                            out_dt, out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w,
+                                            stream), "ql_linear_forward_noalloc")
 
 
 def ql_quantize_groups(x, x_dt, rows, cols, ldx, group_rows, fmt, scale_in, x_q, ldq, scale_out, amax_out,

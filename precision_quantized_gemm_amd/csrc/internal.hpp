@@ -160,6 +160,18 @@ hipError_t launch_amax_finalize(const GemmParams &p, int64_t nblocks, hipStream_
 // fails), the size of a persistent grid of one workgroup per CU.
 int device_cu_count();
 
+// The body of ql_linear_forward (enum arguments as int; the status as int,
+// a ql_status value).  clear_counters: zero the workspace's counter slots
+// (a fill kernel) after validation and before the work.
+int linear_forward_ws(const void *x, int x_dt, int64_t M, int64_t K, const void *w, int64_t N, const void *bias,
+                      int bias_dt, int fmt, const float *sx_in, const float *sw_in, void *out, int out_dt,
+                      const float *out_scale, float *out_amax, void *x_q, float *sx, float *amax_x, void *w_q,
+                      float *sw, float *amax_w, void *ws, bool clear_counters, void *stream);
+
+// Records "what: detail" as the calling thread's last error and returns
+// status (a ql_status value).
+int report_error(int status, const char *what, const char *detail);
+
 // a_fmt / b_fmt: FMT_*; a_mn / b_mn: operand stored MN-major.
 hipError_t launch_qgemm(const GemmParams &p, int a_fmt, int b_fmt, int a_mn, int b_mn, hipStream_t s);
 

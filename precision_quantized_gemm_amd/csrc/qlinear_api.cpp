@@ -330,6 +330,28 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
                             void *w_q, float *sw, float *amax_w,
                             void *ws, void *stream)
 {
+    return (ql_status)ql::linear_forward_ws(x, x_dt, M, K, w, N, bias, bias_dt, fmt, sx_in, sw_in, out, out_dt,
+                                            out_scale, out_amax, x_q, sx, amax_x, w_q, sw, amax_w, ws, false,
+                                            stream);
+}
+
+}  // extern "C"
+
+// Sets the thread's last error (for the entry points in other files).
+int ql::report_error(int status, const char *what, const char *detail)
+{
+    return fail((ql_status)status, "%s: %s", what, detail ? detail : "");
+}
+
+// The body of ql_linear_forward.  clear_counters: after validation, first
+// zero the workspace's counter slots with a fill kernel (for a workspace
+// whose previous contents are not known to be the reset state).
+int ql::linear_forward_ws(const void *x, int x_dt, int64_t M, int64_t K, const void *w, int64_t N,
+                                const void *bias, int bias_dt, int fmt, const float *sx_in, const float *sw_in,
+                                void *out, int out_dt, const float *out_scale, float *out_amax, void *x_q,
+                                float *sx, float *amax_x, void *w_q, float *sw, float *amax_w, void *ws,
+                                bool clear_counters, void *stream)
+{
     if (!ws) return fail(QL_ERR_NULL, "linear_forward: a workspace is required");
     if (!sx || !sw || !amax_x || !amax_w)
         return fail(QL_ERR_NULL, "linear_forward: sx, sw, amax_x and amax_w are required outputs");
@@ -344,6 +366,10 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
     if (st != QL_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (clear_counters) {
+        const hipError_t e = ql::launch_ws_zero(ws, ql::WS_COUNTER_BYTES, s);
+        if (e != hipSuccess) return hip_status(e, "linear_forward: clear the workspace counters");
+    }
     ql::QzParams px = make_qz(x, x_dt, M, K, K, QL_PER_TENSOR, fmt, sx_in, x_q, K, sx, amax_x,
                               ws, ql::WS_SLOT_QA);
     ql::QzParams pw = make_qz(w, x_dt, N, K, K, QL_PER_TENSOR, fmt, sw_in, w_q, K, sw, amax_w,
@@ -354,6 +380,8 @@ ql_status ql_linear_forward(const void *x, ql_dtype x_dt, int64_t M, int64_t K,
     ql::GemmParams pg = make_gemm(g, ql::ws_slot(ws, ql::WS_SLOT_GEMM));
     return hip_status(ql::launch_qgemm(pg, fmt, fmt, 0, 0, s), "linear_forward: qgemm");
 }
+
+extern "C" {
 
 ql_status ql_quantize_groups(const void *x, ql_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx,
                              int64_t group_rows, ql_qfmt fmt, const float *scale_in,

@@ -25,7 +25,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["ql_workspace_bytes", "ql_workspace_init", "ql_quantize", "ql_quantize_ring",
-                                  "ql_qgemm", "ql_linear_forward", "ql_linear_backward", "ql_linear_forward_static",
+                                  "ql_qgemm", "ql_linear_forward", "ql_linear_forward_noalloc", "ql_linear_backward",
+                                  "ql_linear_forward_static",
                                   "ql_quantize_groups", "ql_qgemm_batched", "ql_status_string", "ql_last_error"])
 
 
@@ -272,3 +273,4 @@ def _batched(**kw):
 def test_qgemm_batched_validation(kw, status):
     assert _batched(**kw) == status
     assert q.ql_last_error()
+
