@@ -8,17 +8,26 @@ cast), then the scaled E4M3 GEMM 16384 x 8192 x 8192 with FP32 accumulation
 and E4M3 output (out_scale = amax_prev / 448, amax_prev being the out_amax
 of the previous step on the same inputs), which also publishes the step's
 own out_amax.  The step is one ql_linear_forward call (the quantizes of a
-and b share each pass's launch).  After the timed region the same work runs
-again as its three C-ABI calls (ql_quantize, ql_quantize, ql_qgemm) with
-HIP events between them on the stream they run on, which gives each
-kernel's duration for the roofline and the quantize rates.
+and b share each pass's launch); consecutive steps alternate between two
+copies of the inputs, so no step finds its inputs in the memory-side
+cache.  After W warm-up steps, further untimed steps run until 0.5 s of
+warm-up have passed; then K steps are timed, with an event after each for
+the per-step p10 / p50 / p90.
+
+After the timed region the same work runs again as its three C-ABI calls
+(ql_quantize, ql_quantize, ql_qgemm) with HIP events between them on the
+stream they run on, which gives the GEMM's duration for the roofline.  The
+quantize rates are timed on rotated copies of a and b (768 / 640 MiB) next
+to the memory system's ceiling for the same access pattern
+(ql_stream_probe).
 
 Prints one JSON line.  `value` is the step's GEMM work (2*M*N*K) divided by
 the step time (inputs resident in HBM).  `roofline` is the GEMM kernel
 against the dense FP8 matrix-core peak; `quantize` reports the quantize
-calls against HBM peak; `cpu_baseline` is the oracle (plain C) timed on a
-bounded sample of the same workload on this host's cores and scaled to the
-full step.
+calls against HBM peak and the measured ceiling; `cpu_baseline` is the
+oracle (plain C) timed on a bounded sample of the same workload over this
+host's cores and scaled to the full step; `cpu_baseline_configs` times the
+oracle on the small configurations next to their GPU times.
 
 `--copy-calibration` instead times a plain 1 GiB device copy (the known-size
 kernel that scales the HBM byte counters of a profiler run) and exits.
@@ -58,8 +67,9 @@ def parse():
                     help="time a plain 1 GiB device-to-device copy instead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="output rows in the oracle GEMM sample")
-    ap.add_argument("--cpu-cols", type=int, default=4096, help="output columns in the oracle GEMM sample")
+    ap.add_argument("--cpu-rows", type=int, default=32, help="full output rows in the oracle GEMM sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run the oracle GEMMs of the MLP-up and backward configurations in full (minutes)")
     return ap.parse_args()
 
 
@@ -80,48 +90,132 @@ def time_events(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
-def cpu_baseline(a_cpu, b_cpu, M, N, K, rows, cols):
-    """Oracle timing on a bounded sample, scaled to one full step.
+def host_threads():
+    """Threads for the oracle legs: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when the environment sets it (the host's
+    share of cores for this GPU)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def oracle_quantize_threaded(oracle, x_bits, gran, fmt, pool, threads):
+    """The oracle's quantize of x split over row chunks: per tensor, the
+    amax of every chunk (oracle.amax_raw), then every chunk's cast with the
+    whole tensor's step (oracle.quantize with that step given); per row,
+    each chunk on its own.  Returns the codes."""
+    import numpy as np
+    chunks = [c for c in np.array_split(np.arange(x_bits.shape[0]), threads * 2) if c.size]
+    if gran == oracle.PER_ROW:
+        parts = list(pool.map(lambda c: oracle.quantize(x_bits[c], gran, fmt)[0], chunks))
+        return np.concatenate(parts)
+    amax = max(pool.map(lambda c: float(oracle.amax_raw(x_bits[c], oracle.PER_TENSOR)[0]), chunks))
+    floor = float(oracle.amax_floor(fmt))
+    step = np.float32(max(np.float32(amax), np.float32(floor))) / np.float32(oracle.qmax(fmt))
+    parts = list(pool.map(lambda c: oracle.quantize(x_bits[c], oracle.PER_TENSOR, fmt,
+                                                     scale_in=np.array([step], np.float32))[0], chunks))
+    return np.concatenate(parts)
+
+
+def oracle_gemm_seconds(oracle, pool, threads, a, af, al, b, bf, bl, K, M, N, rows):
+    """Wall time of the oracle's exact GEMM over `rows` output rows (all N
+    columns), the entries split over the threads, and the factor M / rows
+    that scales it to the whole product."""
+    import numpy as np
+    rows = min(rows, M)
+    ms = np.repeat(np.arange(rows), N).astype(np.int64)
+    ns = np.tile(np.arange(N), rows).astype(np.int64)
+    parts = np.array_split(np.arange(ms.size), threads * 4)
+    t0 = time.perf_counter()
+    list(pool.map(lambda i: oracle.qgemm_entries(a, af, al, b, bf, bl, K, ms[i], ns[i], with_bound=False), parts))
+    return time.perf_counter() - t0, M / rows
+
+
+def cpu_baseline(a_cpu, b_cpu, M, N, K, rows, threads):
+    """Oracle timing for the benchmark step, on a bounded sample.
 
     Sample (roughly 10-30 s of host work): the per-tensor E4M3 quantize of
-    the first 4096 rows of a and of b (one thread: the oracle quantize is a
-    single call), and the exact GEMM of `rows` x `cols` outputs over the full
-    K, split over the host's threads.  Step estimate = per-element quantize
-    time x (M*K + N*K) + per-MAC GEMM time x M*N*K.
+    all of a and b (amax of every row chunk, then every chunk's cast with
+    the tensor's step, over `threads` threads), and the exact GEMM of
+    `rows` full output rows (rows x N entries over the full K), over the
+    same threads.  Step estimate = quantize time + GEMM time x M / rows.
     """
+    import oracle
+    from precision_quantized_gemm_amd import synth
+
+    with ThreadPoolExecutor(threads) as pool:
+        xa, xb = synth.bf16_bits(a_cpu), synth.bf16_bits(b_cpu)
+        t0 = time.perf_counter()
+        qa = oracle_quantize_threaded(oracle, xa, oracle.PER_TENSOR, oracle.E4M3, pool, threads)
+        qb = oracle_quantize_threaded(oracle, xb, oracle.PER_TENSOR, oracle.E4M3, pool, threads)
+        tq = time.perf_counter() - t0
+        tg, scale = oracle_gemm_seconds(oracle, pool, threads, qa, 0, 0, qb, 0, 0, K, M, N, rows)
+    step_s = tq + tg * scale
+    return dict(value=2.0 * M * N * K / step_s / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=(f"quantize of all of a and b ({M * K + N * K} elements, {tq:.1f} s) and the exact GEMM "
+                        f"of {rows} full output rows ({rows}x{N} entries x K={K}, {tg:.1f} s, scaled x{scale:g} "
+                        f"to {M} rows), each over {threads} threads; estimate of the whole "
+                        f"{M}x{N}x{K} step"),
+                step_seconds_estimate=step_s,
+                host_cpus_visible=os.cpu_count(),
+                host_cpus_usable=len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None)
+
+
+def oracle_configs(threads, full):
+    """The oracle on the small configurations (seconds per step, the same
+    work as the GPU lines they sit next to).  C1 and C2 run in full; C3's
+    and C4's GEMMs run in full with `full`, else on row slabs scaled to the
+    whole product (labelled)."""
     import numpy as np
 
     import oracle
     from precision_quantized_gemm_amd import synth
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    rows_q = 4096
-    xa = synth.bf16_bits(a_cpu[:rows_q])
-    xb = synth.bf16_bits(b_cpu[:rows_q])
-    t0 = time.perf_counter()
-    qa, sa, _ = oracle.quantize(xa, oracle.PER_TENSOR, oracle.E4M3)
-    qb, sb, _ = oracle.quantize(xb, oracle.PER_TENSOR, oracle.E4M3)
-    tq_wall = time.perf_counter() - t0
-    tq = tq_wall / (2 * rows_q * K)
-    ms = np.repeat(np.arange(rows), cols).astype(np.int64)
-    ns = np.tile(np.arange(cols), rows).astype(np.int64)
-    chunks = np.array_split(np.arange(ms.size), threads * 4)
-
-    def work(idx):
-        oracle.qgemm_entries(qa, 0, 0, qb, 0, 0, K, ms[idx], ns[idx], with_bound=False)
-
-    t0 = time.perf_counter()
+    out = {}
     with ThreadPoolExecutor(threads) as pool:
-        list(pool.map(work, chunks))
-    tg_wall = time.perf_counter() - t0
-    tmac = tg_wall / (ms.size * K)
-    step_s = tq * (M * K + N * K) + tmac * M * N * K
-    return dict(value=2.0 * M * N * K / step_s / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=(f"quantize of the first {rows_q} rows of a and of b ({2 * rows_q * K} elements, "
-                        f"1 thread, {tq_wall:.1f} s) and the exact GEMM of {rows}x{cols} outputs x K={K} "
-                        f"({ms.size * K} MACs, {threads} threads, {tg_wall:.1f} s); scaled to the full "
-                        f"{M}x{N}x{K} step"),
-                step_seconds_estimate=step_s)
+        def leg(name, quantize, gemms):
+            t0 = time.perf_counter()
+            codes = quantize()
+            tq = time.perf_counter() - t0
+            tg, notes = 0.0, []
+            for g in gemms:
+                t, f = g(codes)
+                tg += t * f
+                notes.append("full" if f == 1 else f"{t:.2f} s slab x{f:g}")
+            out[name] = {"oracle_s": round(tq + tg, 4), "quantize_s": round(tq, 4), "gemm_s": round(tg, 4),
+                         "gemm": ", ".join(notes)}
+
+        d = synth.workload("tiny_linear")
+        bits = lambda t: synth.bf16_bits(t)
+        leg("tiny_linear",
+            lambda: [oracle_quantize_threaded(oracle, bits(d["x"]), 0, 0, pool, threads),
+                     oracle_quantize_threaded(oracle, bits(d["w"]), 0, 0, pool, threads)],
+            [lambda c: oracle_gemm_seconds(oracle, pool, threads, c[0], 0, 0, c[1], 0, 0, 128, 512, 128, 512)])
+        d2 = synth.workload("rowwise_int8")
+        leg("rowwise_int8",
+            lambda: [oracle_quantize_threaded(oracle, d2["a"].numpy(), 1, 2, pool, threads),
+                     oracle_quantize_threaded(oracle, d2["b"].numpy(), 1, 2, pool, threads)],
+            [lambda c: oracle_gemm_seconds(oracle, pool, threads, c[0], 2, 0, c[1], 2, 0, 1024, 128, 512, 128)])
+        d3 = synth.workload("mlp_up")
+        leg("mlp_up",
+            lambda: [oracle_quantize_threaded(oracle, bits(d3["x"]), 0, 0, pool, threads),
+                     oracle_quantize_threaded(oracle, bits(d3["w"]), 0, 0, pool, threads)],
+            [lambda c: oracle_gemm_seconds(oracle, pool, threads, c[0], 0, 0, c[1], 0, 0, 1024, 2048, 4096,
+                                           2048 if full else 16)])
+        d4 = synth.workload("mlp_backward")
+        xq = oracle_quantize_threaded(oracle, bits(d4["x"]), 0, 0, pool, threads)
+        wq = oracle_quantize_threaded(oracle, bits(d4["w"]), 0, 0, pool, threads)
+        # dX [2048, 1024] = g [2048, 4096] . W (W read MN-major); dW [4096, 1024]
+        # = g^T . X (both MN-major); the column sums of g for grad_bias.
+        leg("mlp_backward",
+            lambda: [oracle_quantize_threaded(oracle, bits(d4["g"]), 0, 1, pool, threads)],
+            [lambda c: oracle_gemm_seconds(oracle, pool, threads, c[0], 1, 0, wq, 0, 1, 4096, 2048, 1024,
+                                           2048 if full else 8),
+             lambda c: oracle_gemm_seconds(oracle, pool, threads, c[0], 1, 1, xq, 0, 1, 2048, 4096, 1024,
+                                           4096 if full else 16)])
+    return out
 
 
 def time_backward(torch, q, synth, dev, reps):
@@ -382,6 +476,27 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=10):
           flush=True)
 
 
+def stream_ceiling(torch, q, dev, srcs, n_units, dst, sink, reps):
+    """The memory-ceiling probe (ql_stream_probe) over the rotated source
+    buffers: ms per launch reading 32*n_units bytes and writing 16*n_units
+    (dst) or nothing but a 1 MiB sink (read only)."""
+    from precision_quantized_gemm_amd import _lib
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, d, s_ in (("read_2B_write_1B", dst, None), ("read_only", None, sink)):
+        i = [0]
+
+        def run():
+            _lib.ql_stream_probe(srcs[i[0] % len(srcs)].data_ptr(), n_units, None if d is None else d.data_ptr(),
+                              None if s_ is None else s_.data_ptr(), stream)
+            i[0] += 1
+
+        for _ in range(len(srcs)):
+            run()
+        out[name] = time_events(run, reps, torch)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -405,8 +520,13 @@ def main():
     a_cpu, b_cpu = d["a"], d["b"]
     M, K = a_cpu.shape
     N = b_cpu.shape[0]
-    a = a_cpu.to(dev)
-    b = b_cpu.to(dev)
+    # Rotated copies of the inputs (the same values at other addresses), so
+    # that no input is still in the 256 MB memory-side cache when a timed
+    # call reads it: the step alternates between 2 sets of (a, b), 768 MiB;
+    # the quantize rates cycle through 3 copies of a (768 MiB) and 5 of b
+    # (640 MiB).
+    a_sets = [a_cpu.to(dev) for _ in range(3)]
+    b_sets = [b_cpu.to(dev) for _ in range(5)]
     u8 = torch.uint8
     out = torch.empty((M, N), dtype=u8, device=dev)
     x_q = torch.empty((M, K), dtype=u8, device=dev)
@@ -422,115 +542,141 @@ def main():
         return lambda: q.ql_quantize(P(x), _lib.QL_DT_BF16, rows, K, K, 0, 0, None, P(xq), K, P(s), P(am),
                                      P(ws), stream)
 
-    qa, qb = quant(a, M, x_q, sx, amax_x), quant(b, N, w_q, sw, amax_w)
-
     def gemm():
         q.ql_qgemm(P(x_q), 0, 0, K, P(w_q), 0, 0, K, M, N, K, P(sx), 0, P(sw), 0, None, 0,
                    P(out), _lib.QL_DT_E4M3, N, P(out_scale), P(out_amax), P(ws), stream)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        qa()
-        if ev is not None:
-            ev[1].record()
-        qb()
-        if ev is not None:
-            ev[2].record()
-        gemm()
-        if ev is not None:
-            ev[3].record()
-
     # The step: one ql_linear_forward call (quantize a and b per tensor, the
     # quantizes sharing each pass's launch, then the GEMM with E4M3 output
-    # and out_amax).
-    def fused_step():
+    # and out_amax), on input set i % 2.
+    def fused_step(i):
+        a, b = a_sets[i % 2], b_sets[i % 2]
         q.ql_linear_forward(P(a), _lib.QL_DT_BF16, M, K, P(b), N, None, 0, _lib.QL_FMT_E4M3, None, None,
                             P(out), _lib.QL_DT_E4M3, P(out_scale), P(out_amax), P(x_q), P(sx), P(amax_x),
                             P(w_q), P(sw), P(amax_w), P(ws), stream)
 
     log("warmup")
-    fused_step()
+    fused_step(0)
     torch.cuda.synchronize()
     out_scale.copy_(out_amax / 448.0)           # amax_prev / 448
-    for _ in range(max(0, args.warmup - 1)):
-        fused_step()
+    t_w0 = time.perf_counter()
+    done = 1
+    for i in range(1, max(1, args.warmup)):
+        fused_step(i)
+    done = max(1, args.warmup)
     torch.cuda.synchronize()
+    # Then untimed steps until at least 0.5 s of warm-up have passed, so the
+    # clock has settled under this load before the timed region.
+    extra = 0
+    while time.perf_counter() - t_w0 < 0.5:
+        for _ in range(20):
+            fused_step(done + extra)
+            extra += 1
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    e_start.record()
-    for _ in range(args.steps):
-        fused_step()
-    e_end.record()
+    ev[0].record()
+    for i in range(args.steps):
+        fused_step(i)
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    ms_step = e_start.elapsed_time(e_end) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
 
     # Breakdown (after the timed region): the same work as three calls with
     # events between them, for the per-kernel rates and the roofline.
     log("per-call breakdown")
-    for _ in range(2):
-        step()
+
+    def step(i, evs=None):
+        a, b = a_sets[i % 2], b_sets[i % 2]
+        if evs is not None:
+            evs[0].record()
+        quant(a, M, x_q, sx, amax_x)()
+        if evs is not None:
+            evs[1].record()
+        quant(b, N, w_q, sw, amax_w)()
+        if evs is not None:
+            evs[2].record()
+        gemm()
+        if evs is not None:
+            evs[3].record()
+
+    for i in range(4):
+        step(i)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    for ev in events:
-        step(ev)
+    for i, evs in enumerate(events):
+        step(i, evs)
     torch.cuda.synchronize()
     ms_step_calls = events[0][0].elapsed_time(events[-1][3]) / args.steps
-    ms_qa = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
-    ms_qb = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
-    ms_gemm = sum(ev[2].elapsed_time(ev[3]) for ev in events) / args.steps
-    gemm_each = sorted(ev[2].elapsed_time(ev[3]) for ev in events)
-    pct = lambda f: gemm_each[min(len(gemm_each) - 1, int(f * len(gemm_each)))]
+    ms_gemm = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    gemm_each = sorted(e[2].elapsed_time(e[3]) for e in events)
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
-    # Quantize bytes per BF16 element, per-tensor current scaling: the
-    # method reads x twice (amax pass, cast pass) and writes one code byte:
-    # 5 B; the compulsory traffic is 3 B.
-    qa_bytes5, qa_bytes3 = 5.0 * M * K, 3.0 * M * K
-    qb_bytes5 = 5.0 * N * K
-    qa_gbps = qa_bytes5 / (ms_qa * 1e-3) / 1e9
-    qb_gbps = qb_bytes5 / (ms_qb * 1e-3) / 1e9
 
-    # Single-pass delayed scaling through an amax history ring on the same
-    # a (one read of BF16 x, one code byte written: 3 B/elem), timed on its
-    # own after the step.
+    # Quantize rates on rotated inputs (each call reads a copy that the
+    # previous calls have pushed out of the memory-side cache).
+    log("quantize on rotated inputs")
+    reps_q = max(args.steps, 30)
+
+    def rotating(fn_of, n):
+        i = [0]
+
+        def run():
+            fn_of(i[0] % n)()
+            i[0] += 1
+        return run
+
+    qa_rot = rotating(lambda i: quant(a_sets[i], M, x_q, sx, amax_x), len(a_sets))
+    qb_rot = rotating(lambda i: quant(b_sets[i], N, w_q, sw, amax_w), len(b_sets))
+    for _ in range(6):
+        qa_rot(); qb_rot()
+    ms_qa = time_events(qa_rot, reps_q, torch)
+    ms_qb = time_events(qb_rot, reps_q, torch)
+
+    # Single-pass delayed scaling through an amax history ring (one read of
+    # BF16 x, one code byte written: 3 B/elem), on the rotated copies of a.
     ring = torch.zeros(17, dtype=torch.float32, device=dev)
     ring[-1] = 1.0
     su, am = f1(), f1()
     ring_idx = [0]
 
-    def qa_ring():
-        q.ql_quantize_ring(P(a), _lib.QL_DT_BF16, M, K, K, _lib.QL_FMT_E4M3, P(ring), 16, ring_idx[0] % 16, 0,
-                           P(x_q), K, P(su), P(am), P(ws), stream)
-        ring_idx[0] += 1
+    def qa_ring_of(i):
+        def run():
+            q.ql_quantize_ring(P(a_sets[i]), _lib.QL_DT_BF16, M, K, K, _lib.QL_FMT_E4M3, P(ring), 16,
+                               ring_idx[0] % 16, 0, P(x_q), K, P(su), P(am), P(ws), stream)
+            ring_idx[0] += 1
+        return run
 
+    qa_ring = rotating(qa_ring_of, len(a_sets))
     for _ in range(3):
         qa_ring()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        qa_ring()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_ring = e0.elapsed_time(e1) / args.steps
+    ms_ring = time_events(qa_ring, reps_q, torch)
+
+    # The memory system's ceiling for the same traffic (ql_stream_probe on
+    # the same rotated copies of a: 2 B read and 1 B written per element,
+    # and read only).
+    log("streaming ceiling")
+    sink = torch.empty(1 << 20, dtype=u8, device=dev)
+    ceil = stream_ceiling(torch, q, dev, a_sets, M * K // 16, x_q, sink, reps_q)
 
     # Static FP8 inference on the same layer: w arrives quantized (the w_q /
     # sw the step produced), so a call quantizes a and runs the GEMM.
-    def static_step():
-        q.ql_linear_forward_static(P(a), _lib.QL_DT_BF16, M, K, P(w_q), N, P(sw), None, 0, None,
-                                   _lib.QL_FMT_E4M3, None, P(out), _lib.QL_DT_E4M3, P(out_scale), P(out_amax),
-                                   P(x_q), P(sx), P(amax_x), P(ws), stream)
+    def static_step_of(i):
+        return lambda: q.ql_linear_forward_static(P(a_sets[i]), _lib.QL_DT_BF16, M, K, P(w_q), N, P(sw), None, 0,
+                                                  None, _lib.QL_FMT_E4M3, None, P(out), _lib.QL_DT_E4M3,
+                                                  P(out_scale), P(out_amax), P(x_q), P(sx), P(amax_x), P(ws),
+                                                  stream)
 
+    static_step = rotating(static_step_of, len(a_sets))
     for _ in range(3):
         static_step()
     ms_static = time_events(static_step, args.steps, torch)
-
-
 
     # Backward of the MLP-up layer (G [2048, 4096] BF16 -> E5M2, x_q
     # [2048, 1024] and w_q [4096, 1024] E4M3): one ql_linear_backward call
@@ -552,11 +698,28 @@ def main():
     log("shader clock under the GEMM")
     sclk = sclk_under(gemm, torch, 500)
 
-    cpu = None
+    cpu, cpu_cfg = None, None
+    threads = host_threads()
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline(a_cpu, b_cpu, M, N, K, args.cpu_rows, args.cpu_cols)
+        log(f"cpu baseline (oracle, {threads} threads)")
+        cpu = cpu_baseline(a_cpu, b_cpu, M, N, K, args.cpu_rows, threads)
+        log("oracle on the small configurations")
+        cpu_cfg = oracle_configs(threads, args.cpu_full)
+        gpu_ms = {"tiny_linear": small["tiny_linear"]["ms_eager"], "rowwise_int8": small["rowwise_int8"]["ms_eager"],
+                  "mlp_up": small["mlp_up"]["ms_eager"], "mlp_backward": None if bwd is None else bwd["ms_per_call"]}
+        for k, v in cpu_cfg.items():
+            if gpu_ms.get(k):
+                v["gpu_ms"] = gpu_ms[k]
+                v["oracle_over_gpu"] = round(v["oracle_s"] * 1e3 / gpu_ms[k], 1)
 
+    qa_bytes3, qa_bytes5 = 3.0 * M * K, 5.0 * M * K
+    qb_bytes3, qb_bytes5 = 3.0 * N * K, 5.0 * N * K
+    rate = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    ceil_21 = rate(qa_bytes3, ceil["read_2B_write_1B"])
+    ceil_r = rate(2.0 * M * K, ceil["read_only"])
+    # The two-pass quantize at the ceiling: one read-only pass and one
+    # 2:1 pass over a.
+    two_pass_floor_ms = ceil["read_only"] + ceil["read_2B_write_1B"]
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -573,9 +736,13 @@ def main():
         "config": {
             "workload": "large_fp8: quantize a[16384,8192] bf16 Student-t(3) and b[8192,8192] bf16 N(0,1/8192) "
                         "per-tensor E4M3, then E4M3 GEMM 16384x8192x8192 FP32-acc, E4M3 out "
-                        "(out_scale = amax_prev/448); per step one ql_linear_forward (quantize a and b, the GEMM)",
+                        "(out_scale = amax_prev/448); per step one ql_linear_forward (quantize a and b, the GEMM), "
+                        "alternating between 2 copies of the inputs",
             "M": M, "N": N, "K": K, "parallelism": "single GPU",
         },
+        "step_ms_p10_p50_p90": [round(pct(step_each, 0.1), 5), round(pct(step_each, 0.5), 5),
+                                round(pct(step_each, 0.9), 5)],
+        "warmup_extra_steps": extra,
         "roofline": {
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
@@ -585,27 +752,41 @@ def main():
             "traffic": gemm_traffic(),
             "kernel": "qgemm_nt_kernel<E4M3,E4M3> (256x256x128 tiles)",
             "ms_per_launch": round(ms_gemm, 5),
-            "ms_per_launch_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+            "ms_per_launch_p10_p50_p90": [round(pct(gemm_each, 0.1), 5), round(pct(gemm_each, 0.5), 5),
+                                          round(pct(gemm_each, 0.9), 5)],
             "sclk_mhz_under_gemm": sclk,
             "frac_at_measured_sclk": None if not sclk else round(gemm_tflops / (PEAK_FP8_TFLOPS * sclk / 2400.0), 4),
             "per_launch_flops": flops,
         },
         "quantize": {
+            "inputs": "rotated: 3 copies of a (768 MiB), 5 of b (640 MiB); none is in the 256 MB memory-side "
+                      "cache when its call starts",
             "a_ms": round(ms_qa, 5), "b_ms": round(ms_qb, 5),
-            "bytes_per_elem": "5 (two reads of BF16 x, one code byte written)",
-            "a_GBps_5B_per_elem": round(qa_gbps, 1),
-            "a_GBps_3B_per_elem": round(qa_bytes3 / (ms_qa * 1e-3) / 1e9, 1),
-            "b_GBps_5B_per_elem": round(qb_gbps, 1),
-            "a_frac_hbm_peak_5B": round(qa_gbps / PEAK_HBM_GBPS, 4),
+            "a_GBps_3B_per_elem": round(rate(qa_bytes3, ms_qa), 1),
+            "a_GBps_5B_per_elem": round(rate(qa_bytes5, ms_qa), 1),
+            "a_frac_hbm_peak_3B": round(rate(qa_bytes3, ms_qa) / PEAK_HBM_GBPS, 4),
+            "a_frac_of_two_pass_ceiling": round(two_pass_floor_ms / ms_qa, 4),
+            "b_GBps_3B_per_elem": round(rate(qb_bytes3, ms_qb), 1),
+            "b_GBps_5B_per_elem": round(rate(qb_bytes5, ms_qb), 1),
+            "bytes_per_elem": "per-tensor current scaling reads x twice (amax pass, cast pass) and writes one "
+                              "code byte: 5 B; 3 B is the compulsory traffic",
             "a_ring_ms": round(ms_ring, 5),
-            "a_ring_GBps_3B_per_elem": round(qa_bytes3 / (ms_ring * 1e-3) / 1e9, 1),
-            "a_ring_frac_hbm_peak": round(qa_bytes3 / (ms_ring * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "a_ring_note": "ql_quantize_ring (delayed scaling, 16-entry history), back to back on a",
+            "a_ring_GBps_3B_per_elem": round(rate(qa_bytes3, ms_ring), 1),
+            "a_ring_frac_hbm_peak": round(rate(qa_bytes3, ms_ring) / PEAK_HBM_GBPS, 4),
+            "a_ring_frac_of_ceiling": round(rate(qa_bytes3, ms_ring) / ceil_21, 4),
+            "a_ring_note": "ql_quantize_ring (delayed scaling, 16-entry history): one pass, 3 B/elem",
+            "ceiling": {"kernel": "ql_stream_probe (the cast's access pattern, no arithmetic) on the rotated a",
+                        "read_2B_write_1B_GBps": round(ceil_21, 1),
+                        "read_2B_write_1B_ms": round(ceil["read_2B_write_1B"], 5),
+                        "read_only_GBps": round(ceil_r, 1), "read_only_ms": round(ceil["read_only"], 5),
+                        "frac_hbm_peak_2to1": round(ceil_21 / PEAK_HBM_GBPS, 4),
+                        "frac_hbm_peak_read": round(ceil_r / PEAK_HBM_GBPS, 4)},
             "peak_GBps": PEAK_HBM_GBPS,
         },
         "step_as_three_calls": {"ms_per_step": round(ms_step_calls, 5),
                                 "TFLOPs": round(flops / (ms_step_calls * 1e-3) / 1e12, 2),
-                                "workload": "the same step as ql_quantize(a), ql_quantize(b), ql_qgemm with events between"},
+                                "workload": "the same step as ql_quantize(a), ql_quantize(b), ql_qgemm with events "
+                                            "between"},
         "static_inference": {"ms_per_step": round(ms_static, 5),
                              "TFLOPs": round(flops / (ms_static * 1e-3) / 1e12, 2),
                              "workload": "ql_linear_forward_static: quantize a, GEMM with the pre-quantized b"},
@@ -615,6 +796,7 @@ def main():
         "int8_large": int8,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
+        "cpu_baseline_configs": cpu_cfg,
         "wall_s_timed_region": round(t_wall, 4),
     }
     print(json.dumps(line), flush=True)

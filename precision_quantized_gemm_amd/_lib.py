@@ -73,6 +73,8 @@ def load():
     lib.ql_linear_backward.argtypes = [vp, i64, i64, vp, i32, vp, vp, i32, vp, i64, ctypes.c_uint, i32, vp,
                                        vp, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.ql_linear_backward.restype = i32
+    lib.ql_stream_probe.argtypes = [vp, i64, vp, vp, vp]
+    lib.ql_stream_probe.restype = i32
     lib.ql_status_string.argtypes = [i32]
     lib.ql_status_string.restype = ctypes.c_char_p
     lib.ql_last_error.argtypes = []
@@ -162,6 +164,12 @@ def ql_linear_backward(g, M, N, x_q, x_fmt, sx, w_q, w_fmt, sw, K, masks, g_fmt,
                        g_q, sg, amax_g, ws, stream=0) -> None:
     _check(load().ql_linear_backward(g, M, N, x_q, x_fmt, sx, w_q, w_fmt, sw, K, masks, g_fmt, sg_in, dx, dw,
                                      out_dt, dbias, g_q, sg, amax_g, ws, stream), "ql_linear_backward")
+
+
+def ql_stream_probe(src, n_units, dst, sink, stream=0) -> None:
+    """The memory-ceiling probe of include/qlinear_measure.h (a measurement
+    aid outside the method)."""
+    _check(load().ql_stream_probe(src, n_units, dst, sink, stream), "ql_stream_probe")
 
 
 def ql_status_string(status: int) -> str:

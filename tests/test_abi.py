@@ -274,3 +274,17 @@ def test_qgemm_batched_validation(kw, status):
     assert _batched(**kw) == status
     assert q.ql_last_error()
 
+
+def test_stream_probe_validates_before_launch():
+    """The memory-ceiling probe (include/qlinear_measure.h) rejects bad
+    arguments on the host, enqueuing nothing (no GPU needed)."""
+    import precision_quantized_gemm_amd._lib as L
+    with pytest.raises(ValueError):
+        L.ql_stream_probe(16, -1, 32, None)
+    with pytest.raises(ValueError):                 # both dst and sink
+        L.ql_stream_probe(16, 4, 32, 64)
+    with pytest.raises(ValueError):                 # misaligned
+        L.ql_stream_probe(8, 4, 32, None)
+    with pytest.raises(L.QLError):                  # no source
+        L.ql_stream_probe(None, 4, 32, None)
+    L.ql_stream_probe(None, 0, None, None)          # nothing to do

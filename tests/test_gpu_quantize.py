@@ -189,3 +189,21 @@ def test_quantize_ring_sequence(orc, shape, dt, fmt, hist_len):
         assert su.item() == su_ref and am.item() == am_ref, (t, su.item(), su_ref, am.item(), am_ref)
         got_ring = ring.cpu().numpy()
         assert np.array_equal(got_ring.view(np.uint32), ring_ref.view(np.uint32)), (t, got_ring, ring_ref)
+
+
+def test_stream_probe_writes_what_it_reads():
+    """The memory-ceiling probe used by the benchmark reads every byte it
+    is given: dst[u] = src[2u] XOR src[2u+1] (16-byte words), over a ragged
+    number of units and several grid strides."""
+    import precision_quantized_gemm_amd._lib as L
+    n = 256 * 1024 * 5 + 77
+    rng = np.random.default_rng(5)
+    src = rng.integers(0, 2 ** 32, size=(n, 8), dtype=np.uint32)
+    s = torch.from_numpy(src.view(np.int32)).cuda()
+    d = torch.empty((n, 4), dtype=torch.int32, device="cuda")
+    sink = torch.empty(1 << 18, dtype=torch.int32, device="cuda")
+    L.ql_stream_probe(s.data_ptr(), n, d.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+    L.ql_stream_probe(s.data_ptr(), n, None, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = src[:, :4] ^ src[:, 4:]
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), want)
