@@ -239,6 +239,45 @@ def time_backward(torch, q, synth, dev, reps):
             "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
 
 
+def time_mlp_products(torch, q, _lib, synth, dev, reps):
+    """Each product of the MLP-up layer alone (ql_qgemm, BF16 out): the
+    forward x_q . w_q^T + bias (2048 x 4096 x 1024, both K-major), dX =
+    g_q . W (2048 x 1024 x 4096, W read MN-major) and dW = g_q^T . X
+    (4096 x 1024 x 2048, both read MN-major)."""
+    d = synth.workload("mlp_backward")
+    up = synth.workload("mlp_up")
+    P = lambda t: t.data_ptr()
+    fx = q.quantize(up["x"].to(dev), "per_tensor", "e4m3")
+    fw = q.quantize(up["w"].to(dev), "per_tensor", "e4m3")
+    fg = q.quantize(d["g"].to(dev), "per_tensor", "e5m2")
+    bias = up["bias"].to(dev)
+    (xq, sx, _), (wq, sw, _), (gq, sg, _) = fx, fw, fg
+    M, K = xq.shape
+    N = wq.shape[0]
+    stream = torch.cuda.current_stream().cuda_stream
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    E4, E5, KM, MN, BF = _lib.QL_FMT_E4M3, _lib.QL_FMT_E5M2, _lib.QL_K_MAJOR, _lib.QL_MN_MAJOR, _lib.QL_DT_BF16
+    runs = {
+        "forward": (lambda: q.ql_qgemm(P(xq), E4, KM, K, P(wq), E4, KM, K, M, N, K, P(sx), 0, P(sw), 0, P(bias),
+                                       _lib.QL_DT_FP32, P(y), BF, N, None, None, None, stream), (M, N, K)),
+        "dX": (lambda: q.ql_qgemm(P(gq), E5, KM, N, P(wq), E4, MN, K, M, K, N, P(sg), 0, P(sw), 0, None, 0,
+                                  P(dx), BF, K, None, None, None, stream), (M, K, N)),
+        "dW": (lambda: q.ql_qgemm(P(gq), E5, MN, N, P(xq), E4, MN, K, N, K, M, P(sg), 0, P(sx), 0, None, 0,
+                                  P(dw), BF, K, None, None, None, stream), (N, K, M)),
+    }
+    out = {}
+    for name, (run, (m, n, k)) in runs.items():
+        for _ in range(5):
+            run()
+        ms = time_events(run, max(reps, 50), torch)
+        fl = 2.0 * m * n * k
+        out[name] = {"MxNxK": f"{m}x{n}x{k}", "us": round(ms * 1e3, 2), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    return out
+
+
 def time_per_head(torch, q, _lib, synth, dev, reps):
     """The per-head attention products of the per-head workload (BH = 16,
     N = 196, D = 64): per-head E4M3 quantize of q, k, p, v
@@ -686,6 +725,9 @@ def main():
         log("backward")
         bwd = time_backward(torch, q, synth, dev, args.steps)
 
+    log("MLP-up layer products")
+    mlp_products = time_mlp_products(torch, q, _lib, synth, dev, args.steps)
+
     log("per-head batched products")
     per_head = time_per_head(torch, q, _lib, synth, dev, args.steps)
 
@@ -791,6 +833,7 @@ def main():
                              "TFLOPs": round(flops / (ms_static * 1e-3) / 1e12, 2),
                              "workload": "ql_linear_forward_static: quantize a, GEMM with the pre-quantized b"},
         "linear_backward": bwd,
+        "mlp_products": mlp_products,
         "per_head": per_head,
         "small_configs": small,
         "int8_large": int8,

@@ -26,6 +26,7 @@ constexpr uint32_t BUF_OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;   // gfx9 raw-buffer descriptor word 3
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Fused epilogue for 4 consecutive outputs of one row:
 //   v = acc * sa[row|0] * sb[col|0] (+ bias[col]), then the output cast.

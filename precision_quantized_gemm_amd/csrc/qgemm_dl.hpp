@@ -98,7 +98,6 @@ template <int R, bool MN> struct DlOperand {
 // tell which stage they write); completion is awaited explicitly with
 // lgkmcnt, and the destination registers are tied to that wait so that no
 // use is scheduled before it.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 dl_read_b128(uint32_t addr)
 {

@@ -3,6 +3,7 @@
 #include "qgemm_impl.hpp"
 #include "qgemm_nt.hpp"
 #include "qgemm_dl.hpp"
+#include "qgemm_pipe.hpp"
 
 namespace ql {
 
