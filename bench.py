@@ -259,13 +259,14 @@ def time_mlp_products(torch, q, _lib, synth, dev, reps):
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     E4, E5, KM, MN, BF = _lib.QL_FMT_E4M3, _lib.QL_FMT_E5M2, _lib.QL_K_MAJOR, _lib.QL_MN_MAJOR, _lib.QL_DT_BF16
+    ws = P(q.new_workspace(dev))
     runs = {
         "forward": (lambda: q.ql_qgemm(P(xq), E4, KM, K, P(wq), E4, KM, K, M, N, K, P(sx), 0, P(sw), 0, P(bias),
-                                       _lib.QL_DT_FP32, P(y), BF, N, None, None, None, stream), (M, N, K)),
+                                       _lib.QL_DT_FP32, P(y), BF, N, None, None, ws, stream), (M, N, K)),
         "dX": (lambda: q.ql_qgemm(P(gq), E5, KM, N, P(wq), E4, MN, K, M, K, N, P(sg), 0, P(sw), 0, None, 0,
-                                  P(dx), BF, K, None, None, None, stream), (M, K, N)),
+                                  P(dx), BF, K, None, None, ws, stream), (M, K, N)),
         "dW": (lambda: q.ql_qgemm(P(gq), E5, MN, N, P(xq), E4, MN, K, N, K, M, P(sg), 0, P(sx), 0, None, 0,
-                                  P(dw), BF, K, None, None, None, stream), (N, K, M)),
+                                  P(dw), BF, K, None, None, ws, stream), (N, K, M)),
     }
     out = {}
     for name, (run, (m, n, k)) in runs.items():

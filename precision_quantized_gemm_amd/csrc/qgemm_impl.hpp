@@ -455,8 +455,6 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
 template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN>
 hipError_t launch_pipe(GemmParams p, hipStream_t s);
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int STAGES, int MINW>
-hipError_t launch_dl(GemmParams p, hipStream_t s);
 
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)
@@ -472,13 +470,15 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         const int64_t nb = p.batch > 1 ? p.batch : 1;
         const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
         const int64_t t128x64 = ((p.M + 127) / 128) * ((p.N + 63) / 64) * nb;
-        // A single product that still gives every CU a tile of 256 x 128 or
-        // 128 x 128 (but fewer than two of 128 x 128): the pipelined kernel.
+        // A single product that still gives every CU a tile of 256 x 128,
+        // 128 x 128 or 128 x 64 (but fewer than two of 128 x 128): the
+        // pipelined kernel, largest tile first.
         const int64_t cus = device_cu_count();
         if (p.batch <= 1 && p.K > 0 && t128 < 2 * cus) {
             if (((p.M + 255) / 256) * ((p.N + 127) / 128) >= cus)
                 return launch_pipe<AF, BF, A_MN, B_MN, 256, 128>(p, s);
             if (t128 >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 128>(p, s);
+            if (t128x64 >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 64>(p, s);
         }
         if (t128 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 128, 4, 1>(p, s);
         if (t128x64 >= 512) return launch_dl<AF, BF, A_MN, B_MN, 128, 64, 3, 1>(p, s);
@@ -495,6 +495,7 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         if (p.fast && p.batch <= 1 && p.K > 0) {
             if (((p.M + 255) / 256) * ((p.N + 127) / 128) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 256, 128>(p, s);
             if (((p.M + 127) / 128) * ((p.N + 127) / 128) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 128>(p, s);
+            if (((p.M + 127) / 128) * ((p.N + 63) / 64) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 64>(p, s);
         }
         if (p.fast) {
             // The largest tile that still gives every CU a workgroup (batch

@@ -330,7 +330,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu
     // Prologue: steps 0 .. STAGES-1 in flight (one per stage), step 0's
     // half-0 fragments read.
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) issue_load(I0{}, i, 0);
+    for (int i = 0; i < LOADS; ++i) issue_load(I0{}, i, refill_k(0));
     nt_unroll<1, STAGES>([&](auto S) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) issue_load(S, i, refill_k(decltype(S)::value));
@@ -444,8 +444,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN>
 hipError_t launch_pipe(GemmParams p, hipStream_t s)
 {
-    // As many LDS stages as fit (3 of 48 KiB for 256 x 128, 4 of 32 KiB for
-    // 128 x 128): the loads of a step have that many steps to arrive.
+    // As many LDS stages as fit in 128 KiB (3 of 48 KiB for 256 x 128, 4 of
+    // 32 or 24 KiB for 128 x 128 and 128 x 64): the loads of a step have
+    // that many steps to arrive.
     constexpr int STAGES = (BM + BN) * 128 * 4 <= 128 * 1024 ? 4 : 3;
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);

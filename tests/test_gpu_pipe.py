@@ -1,5 +1,6 @@
 """GPU parity of the pipelined kernel for products with few output tiles
-(256 x 128 or 128 x 128 tiles; csrc/qgemm_pipe.hpp) against the oracle.
+(256 x 128, 128 x 128 or 128 x 64 tiles; csrc/qgemm_pipe.hpp) against the
+oracle.
 
 Every shape here gives fewer 256 x 256 tiles than the chip has CUs but at
 least one smaller tile per CU, so it takes that kernel: ragged M and N
@@ -120,3 +121,58 @@ def test_pipe_per_row_and_fp8_out(orc, al, bl):
     differ = check_fp8_out(out8.numpy()[ms, ns], v, S, H, sasb, K, os_, orc, bias=bias_of(bias, ns),
                            what=f"pipe e4m3 {al},{bl}")
     print("pipe e4m3 differing codes:", differ)
+
+
+# 128 x 64 tiles: single products with fewer 128 x 128 tiles than CUs but
+# at least one 128 x 64 tile per CU (the backward's dX shape among them).
+T64 = [(2048, 1024, 4096, 0, 1), (2000, 1040, 2048, 1, 1), (1536, 2304, 1024, 0, 1), (2048, 1024, 4096, 1, 0),
+       (2048, 1024, 4096, 0, 0), (1900, 1104, 1040, 0, 0)]
+
+
+@pytest.mark.parametrize("af,bf", [(1, 0), (0, 0), (2, 2)])
+@pytest.mark.parametrize("shape", T64)
+def test_pipe_128x64(orc, af, bf, shape):
+    M, N, K, al, bl = shape
+    a = finite_codes(orc, 91, af * 2 + al, M, K, af)
+    b = finite_codes(orc, 92, bf * 2 + bl, N, K, bf)
+    a_st, b_st = storage(a, al), storage(b, bl)
+    ms, ns = _entries(M, N, 128, 64, 93)
+    sa, sb = [0.01], [0.02]
+    if af == 2:
+        out = run_gpu(a_st, 2, al, b_st, 2, bl, K, sa, 0, sb, 0, out_dtype="int32")
+        _, _, iacc, _ = orc.qgemm_entries(a_st, 2, al, b_st, 2, bl, K, ms, ns)
+        assert np.array_equal(out.numpy()[ms, ns].astype(np.int64), iacc)
+        return
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, sa, sb)
+    out = run_gpu(a_st, af, al, b_st, bf, bl, K, sa, 0, sb, 0, out_dtype="fp32")
+    again = run_gpu(a_st, af, al, b_st, bf, bl, K, sa, 0, sb, 0, out_dtype="fp32")
+    assert np.array_equal(out.numpy().view(np.uint32), again.numpy().view(np.uint32)), "result not repeatable"
+    print("pipe 128x64", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, what=f"pipe 128x64 {shape} fmt={af},{bf}"))
+
+
+def test_pipe_128x64_epilogues(orc):
+    """128 x 64 tiles with the LDS epilogue (per-row scales, bias, BF16)
+    and with E4M3 output and out_amax."""
+    M, N, K = 2000, 1040, 2048
+    a = finite_codes(orc, 95, 0, M, K, 1)
+    b = finite_codes(orc, 96, 1, N, K, 0)
+    a_st, b_st = storage(a, 0), storage(b, 1)
+    ms, ns = _entries(M, N, 128, 64, 97)
+    sa = (synth.normal(98, 0, M, 0.1).astype(np.float32) ** 2 + 1e-3).astype(np.float32)
+    sb = (synth.normal(98, 1, N, 0.1).astype(np.float32) ** 2 + 1e-3).astype(np.float32)
+    bias = synth.normal(99, 0, N, 0.5)
+    acc, S, _, H, v, sasb = _per_row_entries(orc, a_st, 1, 0, b_st, 0, 1, K, ms, ns, sa, sb, bias)
+    out = run_gpu(a_st, 1, 0, b_st, 0, 1, K, sa, 1, sb, 1, bias=bias, out_dtype="bf16")
+    print("128x64 per-row", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, bias=bias_of(bias, ns),
+                                        what="128x64 per-row"))
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, a_st, 1, 0, b_st, 0, 1, K, ms, ns, [0.003], [0.002])
+    v = v + bias.astype(np.float64)[ns]
+    out32, amax = run_gpu(a_st, 1, 0, b_st, 0, 1, K, [0.003], 0, [0.002], 0, bias=bias, out_dtype="fp32",
+                          out_amax=True)
+    assert amax == np.abs(out32.numpy()).max()
+    os_ = np.float32(amax / 448.0)
+    out8, amax8 = run_gpu(a_st, 1, 0, b_st, 0, 1, K, [0.003], 0, [0.002], 0, bias=bias, out_dtype="e4m3",
+                          out_scale=os_, out_amax=True)
+    assert amax8 == amax
+    print("128x64 e4m3 differing codes:", check_fp8_out(out8.numpy()[ms, ns], v, S, H, sasb, K, os_, orc,
+                                                        bias=bias_of(bias, ns), what="128x64 e4m3"))
