@@ -453,7 +453,7 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
 // gives one per CU (unaligned operands: 128 x 128).  p.fast selects the
 // branch-free buffer-load staging.
 template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN>
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int OCC = 1>
 hipError_t launch_pipe(GemmParams p, hipStream_t s);
 
 template <int AF, int BF, bool A_MN, bool B_MN>
@@ -493,6 +493,9 @@ hipError_t launch_layout(const GemmParams &p, hipStream_t s)
         // 128 x 128) tile per CU: the pipelined kernel with smaller tiles.
         const int64_t cus = device_cu_count();
         if (p.fast && p.batch <= 1 && p.K > 0) {
+            // Two or more 128 x 128 tiles per CU: two workgroups per CU.
+            if (((p.M + 127) / 128) * ((p.N + 127) / 128) >= 2 * cus)
+                return launch_pipe<AF, BF, A_MN, B_MN, 128, 128, 2>(p, s);
             if (((p.M + 255) / 256) * ((p.N + 127) / 128) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 256, 128>(p, s);
             if (((p.M + 127) / 128) * ((p.N + 127) / 128) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 128>(p, s);
             if (((p.M + 127) / 128) * ((p.N + 63) / 64) >= cus) return launch_pipe<AF, BF, A_MN, B_MN, 128, 64>(p, s);

@@ -191,10 +191,10 @@ template <int R, bool MN, int PART> struct PipeOp {
     }
 };
 
-// One wave per SIMD (the LDS stages allow one workgroup per CU), so the
-// register allocator may use the whole register file.
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int STAGES, bool KTAIL>
-__global__ __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_pipe_kernel(
+// OCC workgroups per CU (their LDS stages must fit together), so the
+// register allocator may use 1/OCC of the register file.
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int STAGES, bool KTAIL, int OCC>
+__global__ __launch_bounds__(GEMM_THREADS, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void qgemm_pipe_kernel(
     GemmParams p)
 {
     typedef Mma32<BF, AF> MMA;                 // operands swapped: acc holds C^T
@@ -441,22 +441,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu
     if (p.out_amax) gemm_publish_amax(p, vmax, red);
 }
 
-template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN>
+// OCC = 1: one workgroup per CU with as many LDS stages as fit in 128 KiB
+// (3 of 48 KiB for 256 x 128, 4 of 32 or 24 KiB for 128 x 128 and
+// 128 x 64), so the loads of a step have that many steps to arrive.
+// OCC = 2: two workgroups per CU with 2 stages each, so one workgroup's
+// matrix ops run while the other waits (measured faster on the MLP-up
+// forward, 2048 x 4096 x 1024 in 128 x 128 tiles, and slower on dW).
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int OCC>
 hipError_t launch_pipe(GemmParams p, hipStream_t s)
 {
-    // As many LDS stages as fit in 128 KiB (3 of 48 KiB for 256 x 128, 4 of
-    // 32 or 24 KiB for 128 x 128 and 128 x 64): the loads of a step have
-    // that many steps to arrive.
-    constexpr int STAGES = (BM + BN) * 128 * 4 <= 128 * 1024 ? 4 : 3;
+    constexpr int STAGES = OCC == 2 ? 2 : ((BM + BN) * 128 * 4 <= 128 * 1024 ? 4 : 3);
+    static_assert(OCC * STAGES * (BM + BN) * 128 <= 160 * 1024, "LDS stages of the resident workgroups");
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
     if (p.K % 128 == 0)
-        hipLaunchKernelGGL((qgemm_pipe_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((qgemm_pipe_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, false, OCC>), dim3((unsigned)grid),
                            dim3(GEMM_THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((qgemm_pipe_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((qgemm_pipe_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, true, OCC>), dim3((unsigned)grid),
                            dim3(GEMM_THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.out_amax || !p.amax_part) return e;

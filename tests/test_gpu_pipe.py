@@ -39,10 +39,11 @@ def _per_row_entries(orc, a_st, af, al, b_st, bf, bl, K, ms, ns, sa, sb, bias):
     return acc, S, iacc, H, v, sasb
 
 
-# (M, N, K, tile): 256 x 128 tiles for K-major pairs with >= 256 of them,
-# 128 x 128 otherwise.
-KMAJOR = [(2100, 4000, 1040, (256, 128)), (2048, 4096, 1024, (256, 128)), (2000, 2100, 512, (128, 128)),
-          (2064, 4112, 384, (256, 128))]
+# (M, N, K, tile): K-major pairs take 128 x 128 tiles, two workgroups per
+# CU, with at least two such tiles per CU; else 256 x 128 tiles with one per
+# CU; else 128 x 128.
+KMAJOR = [(2100, 4000, 1040, (128, 128)), (2048, 4096, 1024, (128, 128)), (2000, 2100, 512, (128, 128)),
+          (2064, 4112, 384, (128, 128)), (1920, 4000, 1024, (256, 128)), (1920, 4000, 1040, (256, 128))]
 
 
 @pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (2, 2)])
@@ -92,15 +93,16 @@ def test_pipe_mn_major(orc, af, bf, shape):
     print("pipe mn", check_float(out_values(out)[ms, ns], v, S, H, sasb, K, what=f"pipe mn {shape} fmt={af},{bf}"))
 
 
-@pytest.mark.parametrize("al,bl", [(0, 0), (1, 1)])
-def test_pipe_per_row_and_fp8_out(orc, al, bl):
+@pytest.mark.parametrize("al,bl,M", [(0, 0, 1920), (1, 1, 1920), (0, 0, 2100)])
+def test_pipe_per_row_and_fp8_out(orc, al, bl, M):
     """Per-row scales take the LDS epilogue with its bounds checks; E4M3
-    output with a bias and out_amax takes the register one."""
-    M, N, K = 1920, 4000, 768
+    output with a bias and out_amax takes the register one (256 x 128 tiles,
+    and 128 x 128 tiles two workgroups per CU for M = 2100)."""
+    N, K = 4000, 768
     a = finite_codes(orc, 81, al, M, K, 0)
     b = finite_codes(orc, 82, bl, N, K, 0)
     a_st, b_st = storage(a, al), storage(b, bl)
-    ms, ns = _entries(M, N, 256, 128, 83)
+    ms, ns = _entries(M, N, 256 if M < 2048 else 128, 128, 83)
     sa = (synth.normal(84, 0, M, 0.1).astype(np.float32) ** 2 + 1e-3).astype(np.float32)
     sb = (synth.normal(84, 1, N, 0.1).astype(np.float32) ** 2 + 1e-3).astype(np.float32)
     bias = synth.normal(85, 0, N, 0.5)
