@@ -86,10 +86,11 @@ typedef enum { QL_K_MAJOR = 0, QL_MN_MAJOR = 1 } ql_layout;
  * and never again (the zero-fill dispatch per quantize that [FP8PY]'s commit
  * message removes is not needed at all).  Behind those words the workspace
  * holds scratch that every use overwrites: 1 MiB for grad_bias's partial
- * column sums and 256 KiB for the per-workgroup maxima of a GEMM's
- * out_amax (reduced by a one-workgroup kernel after the GEMM, which keeps
- * the GEMM's workgroups free of device-scope synchronization).  Calls that
- * share a workspace must be ordered (same stream or explicit events);
+ * column sums and 256 KiB for per-workgroup maxima (those of a large
+ * quantize's amax pass, which its cast pass reduces, and those of a GEMM of
+ * more than 512 workgroups, whose out_amax a one-workgroup kernel reduces
+ * after it; smaller GEMM grids elect their last workgroup instead).  Calls
+ * that share a workspace must be ordered (same stream or explicit events);
  * concurrent calls need separate workspaces.
  * ---------------------------------------------------------------------- */
 

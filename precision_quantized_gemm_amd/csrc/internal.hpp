@@ -63,9 +63,9 @@ struct QzParams {
     int64_t hist_len, ring_idx;
     int margin;
     float *scale_used;
-    // Current scaling: workgroup w of the amax pass stores its maximum at
-    // amax_part[w] and a one-workgroup kernel publishes amax and the step
-    // (null: the last-workgroup election).
+    // Current scaling on large grids: workgroup w of the amax pass stores
+    // its maximum at amax_part[w] and every workgroup of the cast pass
+    // reduces them (null: the last-workgroup election).
     uint32_t *amax_part;
 };
 
@@ -134,7 +134,7 @@ struct GemmParams {
     uint32_t *ws;                   // workspace slot for the out_amax election
     // out_amax without an election: workgroup w stores its maximum at
     // amax_part[w] and a one-workgroup kernel reduces them after the GEMM
-    // (null: the election, for grids larger than the array).
+    // (null: the last-workgroup election; see gemm_amax_parts).
     uint32_t *amax_part;
     int a_aligned, b_aligned;       // 16-byte loads allowed
     int out_vec4;                   // 4 consecutive outputs may be stored as one vector
@@ -155,6 +155,18 @@ inline void finish_groups(GemmParams &p)
 // out_amax of a GEMM whose nblocks workgroups stored their maxima at
 // p.amax_part (run right after the GEMM on the same stream).
 hipError_t launch_amax_finalize(const GemmParams &p, int64_t nblocks, hipStream_t s);
+
+// Grids of at most this many workgroups (one wave of them on 256 CUs at two
+// per CU) publish out_amax by the last-workgroup election; the election's
+// atomics are serialized at the memory side, and in a grid that runs in
+// several waves each wave's workgroups would hold their CUs while they
+// queue.  Larger grids (and grids larger than the workspace array) keep
+// per-workgroup maxima and the finalize launch.
+constexpr int64_t GEMM_ELECT_MAX_BLOCKS = 512;
+inline uint32_t *gemm_amax_parts(uint32_t *parts, int64_t blocks)
+{
+    return blocks <= GEMM_ELECT_MAX_BLOCKS || blocks > WS_AMAX_PARTS ? nullptr : parts;
+}
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails), the size of a persistent grid of one workgroup per CU.

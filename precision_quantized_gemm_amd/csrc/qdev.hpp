@@ -187,29 +187,47 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 // Last-workgroup election over a 2-word workspace slot {amax bits, counter}.
 //
 // Every workgroup folds its maximum into slot[0] with a device-scope atomic
-// max, then increments slot[1] with an acquire-release device-scope atomic.
-// The workgroup that sees the count reach the grid size - 1 is the last one: the
-// release/acquire pair orders every other workgroup's max before its read,
-// across all XCDs (their L2s are not coherent without device-scope
-// ordering).  It returns the final maximum and leaves the slot zeroed for the
-// next call, so no separate clearing launch is ever needed.  Only thread 0
-// of each workgroup calls this; it returns true (and *result) in the last.
+// max and, once that has returned, increments slot[1]; the workgroup that
+// sees the count reach `count` - 1 is the last one and reads the maximum
+// back with one more read-modify-write issued after its increment returned.
+// Device-scope read-modify-writes are performed at the memory side, one
+// order per address for every XCD, and each one here is issued only after
+// the previous one of the same workgroup has completed, so the last read
+// comes after every workgroup's max.  All of them are relaxed: no
+// workgroup's other stores are ordered by the election, only the maximum
+// that travels through the atomics is, and no L2 is written back or
+// invalidated (an acquire-release increment would do both, which costs
+// the streaming kernels a write-back of their dirty output per workgroup).
+// The last workgroup leaves the slot zeroed for the next call (the kernel's
+// end makes those stores visible to later launches), so no clearing launch
+// is ever needed.  Only thread 0 of each workgroup calls this; it returns
+// true (and *result) in the last.
 //
 // Cost: read-modify-writes on one address are serialized by the memory
-// system (about 10 ns each on MI355X), and the acquire-release increment
-// also writes back and invalidates the XCD's L2.  Grids that finish all at
-// once (the streaming quantize kernels) therefore stay at a few hundred
-// workgroups.  `count` is the number of workgroups that take part (a grid
-// row, when the rows of a grid are independent elections).
+// system (about 10 ns each on MI355X), so the grids that elect stay at a
+// few hundred workgroups finishing together.  `count` is the number of
+// workgroups that take part (a grid row, when the rows of a grid are
+// independent elections).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v)
+{
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(v));    // hides the value from the compiler
+    return v;
+}
+
 __device__ __forceinline__ bool elect_last_max_n(uint32_t *slot, uint32_t block_max, uint32_t *result,
                                                  uint32_t count)
 {
-    __hip_atomic_fetch_max(&slot[0], block_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t prev = __hip_atomic_fetch_add(&slot[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t before = __hip_atomic_fetch_max(&slot[0], block_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" : : "v"(before) : "memory");               // the max has returned
+    const uint32_t prev = __hip_atomic_fetch_add(&slot[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" : : "v"(prev) : "memory");                 // the increment has returned
     if (prev != count - 1) return false;
-    *result = __hip_atomic_load(&slot[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    // max with an opaque zero: a read-modify-write the compiler cannot turn into a load
+    const uint32_t m = __hip_atomic_fetch_max(&slot[0], opaque_u32(0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" : : "v"(m) : "memory");
+    *result = m;
     __hip_atomic_store(&slot[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&slot[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&slot[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
 

@@ -131,10 +131,8 @@ struct Epilogue {
 
 // End of a GEMM workgroup's out_amax: the workgroup maximum goes to its
 // own slot of p.amax_part (reduced by a small kernel after the GEMM), or,
-// without that array, into the last-workgroup election.  The election's
-// device-scope acquire-release increment writes back and invalidates the
-// XCD's L2, which in a grid of short-lived tiles throws away the operand
-// panels the other tiles of that XCD are reusing.
+// without that array, into the last-workgroup election (grids of one wave:
+// no launch after the GEMM).
 __device__ __forceinline__ void gemm_publish_amax(const GemmParams &p, uint32_t vmax, uint32_t *red)
 {
     vmax = block_max_u32(vmax, red);

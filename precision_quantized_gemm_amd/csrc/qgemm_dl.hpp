@@ -298,7 +298,7 @@ hipError_t launch_dl(GemmParams p, hipStream_t s)
     if (p.tiles_m == 0 || p.tiles_n == 0) p.tiles_m = p.tiles_n = 1;   // as launch_tile: out_amax = 0
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
-    if (grid * batch > WS_AMAX_PARTS) p.amax_part = nullptr;
+    p.amax_part = gemm_amax_parts(p.amax_part, grid * batch);
     hipLaunchKernelGGL((qgemm_dl_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, MINW>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();

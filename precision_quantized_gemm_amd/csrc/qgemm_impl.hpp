@@ -440,7 +440,7 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
     }
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     const unsigned batch = p.batch > 1 ? (unsigned)p.batch : 1u;
-    if (grid * batch > WS_AMAX_PARTS) p.amax_part = nullptr;
+    p.amax_part = gemm_amax_parts(p.amax_part, grid * batch);
     hipLaunchKernelGGL((qgemm_kernel<AF, BF, A_MN, B_MN, BM, BN, MINW, FAST, PF>), dim3((unsigned)grid, batch),
                        dim3(GEMM_THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
@@ -455,6 +455,8 @@ hipError_t launch_tile(GemmParams p, hipStream_t s)
 template <int AF, int BF> hipError_t launch_nt(GemmParams p, hipStream_t s);
 template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int OCC = 1>
 hipError_t launch_pipe(GemmParams p, hipStream_t s);
+template <int AF, int BF, bool A_MN, bool B_MN, int BM, int BN, int STAGES, int MINW>
+hipError_t launch_dl(GemmParams p, hipStream_t s);
 
 template <int AF, int BF, bool A_MN, bool B_MN>
 hipError_t launch_layout(const GemmParams &p, hipStream_t s)

@@ -644,7 +644,7 @@ hipError_t launch_nt(GemmParams p, hipStream_t s)
                        ((p.sa_group == 0 && p.sb_group == 0) || p.out_dt == DT_INT32) && p.out_vec16 &&
                        p.bias_vec16 && tiles > cus;
     const int64_t grid = chain ? cus : tiles;
-    if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
+    p.amax_part = gemm_amax_parts(p.amax_part, grid);
     if (chain)
         hipLaunchKernelGGL((qgemm_nt_kernel<AF, BF, false, true>), dim3((unsigned)grid), dim3(GEMM_THREADS), 0, s, p);
     else if (p.K % NT_BK == 0)

@@ -455,7 +455,7 @@ hipError_t launch_pipe(GemmParams p, hipStream_t s)
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    if (grid > WS_AMAX_PARTS) p.amax_part = nullptr;
+    p.amax_part = gemm_amax_parts(p.amax_part, grid);
     if (p.K % 128 == 0)
         hipLaunchKernelGGL((qgemm_pipe_kernel<AF, BF, A_MN, B_MN, BM, BN, STAGES, false, OCC>), dim3((unsigned)grid),
                            dim3(GEMM_THREADS), 0, s, p);

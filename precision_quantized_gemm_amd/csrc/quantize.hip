@@ -16,13 +16,12 @@
 //             amax and the step, on large ones each workgroup leaves its
 //             maximum in the workspace.
 //   qz_cast   pass 2 (or the only pass under delayed scaling, where it also
-//             measures amax and publishes it from its last workgroup, or
-//             through per-workgroup maxima and qz_publish_parts).  As pass 2
-//             after per-workgroup maxima, every workgroup reduces them and
-//             workgroup 0 publishes amax and the step.  As
-//             pass 2 it walks the tensor from the end backwards, so it
-//             starts on the data pass 1 read last, which the memory-side
-//             cache (256 MB) still holds.
+//             measures amax and publishes it, or updates the history ring,
+//             from its last workgroup).  As pass 2 after per-workgroup
+//             maxima, every workgroup reduces them and workgroup 0
+//             publishes amax and the step.  As pass 2 it walks the tensor
+//             from the end backwards, so it starts on the data pass 1 read
+//             last, which the memory-side cache (256 MB) still holds.
 //   qz_rows   per-row and row groups: one workgroup per group of rows
 //             (one row for per-row scales); the group's second read hits
 //             the cache, so HBM sees each element once.
@@ -50,10 +49,10 @@ __device__ __forceinline__ void store16_nt(uint8_t *dst, uint4 c)
 constexpr int QZ_THREADS = 1024;
 constexpr int QZ_MAX_BLOCKS = 256;
 static_assert(QZ_MAX_BLOCKS <= QZ_PARTS_PER_SLOT, "one workspace maximum per workgroup");
-// Whole-tensor amax passes of at least this many workgroups publish through
-// per-workgroup maxima and a one-workgroup kernel rather than the
-// last-workgroup election, whose acquire-release atomics write back and
-// invalidate each XCD's L2.
+// Current scaling: amax passes of at least this many workgroups leave one
+// maximum per workgroup in the workspace, which every workgroup of the cast
+// pass reduces at its start (no election at the end of pass 1); smaller
+// grids elect the last workgroup, which publishes before the cast starts.
 constexpr int QZ_PARTS_MIN_BLOCKS = 64;
 // Per-row / row-group kernel: one workgroup of 4 waves per group of rows.
 constexpr int QZ_ROW_THREADS = 256;
@@ -346,10 +345,6 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_cast(QzPack pk)
         __shared__ uint32_t last_bits;
         __shared__ int is_last;
         m = block_max_u32(m, red);
-        if (p.amax_part) {                                  // published by qz_publish_parts
-            if (threadIdx.x == 0) p.amax_part[blockIdx.x] = m;
-            return;
-        }
         if (threadIdx.x == 0) {
             uint32_t bits = 0;
             const bool last = elect_last_max_n(p.ws, m, &bits, gridDim.x);
@@ -503,21 +498,6 @@ static int blocks_for(int64_t work)
     return (int)b;
 }
 
-// Publishes grid row y's tensor from the nblocks workgroup maxima of its
-// measuring cast (delayed scaling: amax and the measured step, or the ring
-// update).  Current scaling needs no such launch: its cast pass reduces the
-// amax pass's maxima itself.
-__global__ __launch_bounds__(1024) void qz_publish_parts(QzPack pk, int nblocks)
-{
-    const QzParams &p = pk.t[blockIdx.y];
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nblocks; i += 1024) m = p.amax_part[i] > m ? p.amax_part[i] : m;
-    __shared__ uint32_t red[1024 / 64];
-    m = block_max_u32(m, red);
-    if (p.ring) ring_publish(p, m, red);                 // block-uniform branch
-    else if (threadIdx.x == 0) publish(p, m, 0);
-}
-
 static int64_t tensor_work(const QzParams &p, int mode)
 {
     return mode == MODE_SCALAR ? p.n_elems : (p.n_units > 0 ? p.n_units : p.n_elems);
@@ -531,14 +511,11 @@ static hipError_t launch_tensor_pack(const QzPack &pk_in, int ntensors, hipStrea
     int64_t work = tensor_work(pk_in.t[0], MODE);
     if (ntensors > 1 && tensor_work(pk_in.t[1], MODE) > work) work = tensor_work(pk_in.t[1], MODE);
     const dim3 grid(blocks_for(work), ntensors);
-    // Small grids keep the election: a few atomics cost less than the
-    // publishing launch.
+    // Delayed scaling is one launch: its last workgroup publishes.
     QzPack pk = pk_in;
-    if (grid.x < QZ_PARTS_MIN_BLOCKS) pk.t[0].amax_part = pk.t[1].amax_part = nullptr;
+    if (grid.x < QZ_PARTS_MIN_BLOCKS || pk.t[0].delayed) pk.t[0].amax_part = pk.t[1].amax_part = nullptr;
     if (pk.t[0].delayed) {
         hipLaunchKernelGGL((qz_cast<T, FMT, MODE, true>), grid, dim3(QZ_THREADS), 0, s, pk);
-        if (pk.t[0].amax_part)
-            hipLaunchKernelGGL(qz_publish_parts, dim3(1, ntensors), dim3(1024), 0, s, pk, (int)grid.x);
     } else {
         // With per-workgroup maxima the cast reduces them and publishes.
         hipLaunchKernelGGL((qz_amax<T, MODE>), grid, dim3(QZ_THREADS), 0, s, pk);

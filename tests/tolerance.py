@@ -61,6 +61,7 @@ def strict_bound(v_ref, S, sa_sb):
 def check_float(gpu, v_ref, S, H, sa_sb, K, bias=None, fp8=True, what=""):
     """Assert |gpu - v_ref| <= float_bound; return a small report dict."""
     gpu = np.asarray(gpu, dtype=np.float64)
+    v_ref = np.asarray(v_ref, dtype=np.float64)
     err = np.abs(gpu - v_ref)
     bound = float_bound(v_ref, S, H, sa_sb, K, bias, fp8)
     bad = np.nonzero(~(err <= bound))[0]
@@ -71,11 +72,14 @@ def check_float(gpu, v_ref, S, H, sa_sb, K, bias=None, fp8=True, what=""):
             + ", ".join(f"[{j}] gpu={gpu[j]!r} ref={v_ref[j]!r} err={err[j]:.3g} bound={bound[j]:.3g}" for j in i))
     sb = strict_bound(v_ref, S, sa_sb)
     strict = err <= sb
-    ulps = err / ulp_bf16(v_ref)
+    # error in BF16 ulps of the reference, over nonzero references (an exact
+    # zero has no ulp of its own scale)
+    nz = v_ref != 0
+    ulps = err[nz] / ulp_bf16(v_ref[nz])
     rep = dict(n=int(err.size), strict_fraction=float(strict.mean()) if err.size else 1.0,
                max_err_over_strict=float((err / sb).max()) if err.size else 0.0,
                max_err_over_bound=float((err / bound).max()) if err.size else 0.0,
-               mean_err_ulps=float(ulps.mean()) if err.size else 0.0)
+               mean_err_ulps=float(ulps.mean()) if ulps.size else 0.0)
     record(what, rep)
     return rep
 
