@@ -101,7 +101,9 @@ __device__ __forceinline__ uint32_t encode4<FMT_E4M3>(float a, float b, float c,
     b = __builtin_fminf(__builtin_fmaxf(b, -m), m);
     c = __builtin_fminf(__builtin_fmaxf(c, -m), m);
     d = __builtin_fminf(__builtin_fmaxf(d, -m), m);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // The first convert writes the low half of a register whose high half
+    // the second one overwrites: start from a's bits, not a zeroed register.
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -114,7 +116,9 @@ __device__ __forceinline__ uint32_t encode4<FMT_E5M2>(float a, float b, float c,
     b = __builtin_fminf(__builtin_fmaxf(b, -m), m);
     c = __builtin_fminf(__builtin_fmaxf(c, -m), m);
     d = __builtin_fminf(__builtin_fmaxf(d, -m), m);
-    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    // The first convert writes the low half of a register whose high half
+    // the second one overwrites: start from a's bits, not a zeroed register.
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, __builtin_bit_cast(int, a), false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
     return (uint32_t)w;
 }

@@ -154,6 +154,52 @@ __device__ __forceinline__ void nt_wait_parts(u32x4 (&v)[16])
 }
 
 
+// E4M3 output without bias for 16 consecutive accumulators of one row: the
+// codes are the accumulators times RN(sa*sb / out_scale), and out_amax is
+// max |acc| times |sa*sb| once per workgroup (rounding is monotone, so that
+// is max |RN(acc*sa*sb)|); this keeps max |acc| in macc.
+template <bool INT_ACC>
+__device__ __forceinline__ uint4 nt_e4m3_codes16(const Epilogue &epi, const uint4 (&w)[4], float &macc)
+{
+    auto val = [](uint32_t x) { return INT_ACC ? (float)(int32_t)x : __uint_as_float(x); };
+    float a[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a[4 * q + 0] = val(w[q].x); a[4 * q + 1] = val(w[q].y);
+        a[4 * q + 2] = val(w[q].z); a[4 * q + 3] = val(w[q].w);
+    }
+    // max |a| three operands per instruction: five over 15 values, three
+    // more folding them, the 16th and the running maximum.
+    auto mx3 = [](float x, float y, float z) {
+        return __builtin_elementwise_maximum(x, __builtin_elementwise_maximum(y, z));
+    };
+    float t[5];
+#pragma unroll
+    for (int g = 0; g < 5; ++g)
+        t[g] = mx3(__builtin_fabsf(a[3 * g]), __builtin_fabsf(a[3 * g + 1]), __builtin_fabsf(a[3 * g + 2]));
+    float m = mx3(macc, t[0], t[1]);
+    m = mx3(m, t[2], t[3]);
+    macc = mx3(m, t[4], __builtin_fabsf(a[15]));
+    const float s = epi.s_out;
+    uint4 c;
+    c.x = encode4<FMT_E4M3>(a[0] * s, a[1] * s, a[2] * s, a[3] * s);
+    c.y = encode4<FMT_E4M3>(a[4] * s, a[5] * s, a[6] * s, a[7] * s);
+    c.z = encode4<FMT_E4M3>(a[8] * s, a[9] * s, a[10] * s, a[11] * s);
+    c.w = encode4<FMT_E4M3>(a[12] * s, a[13] * s, a[14] * s, a[15] * s);
+    return c;
+}
+
+// Position of 16-byte chunk c of row r in a wave's 32-row x 128-byte line
+// staging area (E4M3 epilogue): c ^ g(r).  Writes (lane l: row l % 32,
+// chunk 2j + l / 32) and reads (lane l: row 8k + l / 8, chunk l % 8) then
+// put the lanes that share an LDS clock on distinct 16-byte bank slots.
+__device__ __forceinline__ int nt_line_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 3) & 3); }
+
+__device__ __forceinline__ void nt_store16_stream(uint8_t *dst, uint4 c)
+{
+    __builtin_nontemporal_store(u32x4{c.x, c.y, c.z, c.w}, reinterpret_cast<u32x4 *>(dst));
+}
+
 // Fast-path epilogue of 16 consecutive accumulators of one row (per-tensor
 // scales or raw INT32 output, column a multiple of 16, output and bias rows
 // 16-byte aligned, all 16 inside the output): v = acc * sa * sb (+ bias),
@@ -166,29 +212,8 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
                                                int64_t row, int64_t col, uint32_t vmax, float &macc)
 {
     if constexpr (OD == DT_E4M3 && !HB) {
-        // No bias: the codes are the accumulators times RN(sa*sb /
-        // out_scale), and out_amax is max |acc| times |sa*sb| once per
-        // workgroup (rounding is monotone, so that is max |RN(acc*sa*sb)|);
-        // this keeps max |acc| in macc.
-        auto val = [](uint32_t x) { return INT_ACC ? (float)(int32_t)x : __uint_as_float(x); };
-        float a[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            a[4 * q + 0] = val(w[q].x); a[4 * q + 1] = val(w[q].y);
-            a[4 * q + 2] = val(w[q].z); a[4 * q + 3] = val(w[q].w);
-        }
-        float m = macc;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2)
-            m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_fabsf(a[e]), __builtin_fabsf(a[e + 1])));
-        macc = m;
-        const float s = epi.s_out;
-        uint4 c;
-        c.x = encode4<FMT_E4M3>(a[0] * s, a[1] * s, a[2] * s, a[3] * s);
-        c.y = encode4<FMT_E4M3>(a[4] * s, a[5] * s, a[6] * s, a[7] * s);
-        c.z = encode4<FMT_E4M3>(a[8] * s, a[9] * s, a[10] * s, a[11] * s);
-        c.w = encode4<FMT_E4M3>(a[12] * s, a[13] * s, a[14] * s, a[15] * s);
-        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + row * p.ldo + col) = c;
+        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + row * p.ldo + col) =
+            nt_e4m3_codes16<INT_ACC>(epi, w, macc);
         return vmax;
     }
     if constexpr (INT_ACC && OD == DT_INT32) {
@@ -284,6 +309,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     constexpr int WM = NT_BM / 2, WN = NT_BN / 2, TM = WM / 32, TN = WN / 32;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NT_STAGES * NT_STAGE_BYTES];
     __shared__ uint32_t red[GEMM_THREADS / 64];
+    // E4M3 register epilogue: each wave turns a row of blocks (32 rows x
+    // 128 bytes of codes) into whole 128-byte lines here.
+    __shared__ __attribute__((aligned(16))) uint8_t ep_lines[(GEMM_THREADS / 64) * 32 * 128];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar LDS windows
@@ -394,6 +422,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
     // The panels refills load from (this tile's, then the next one's).
     const uint8_t *pa = p.a, *pb = p.b;
     int na = 0, nb = 0;
+
+    // The epilogue's scalars (product scale, output scale) are read once,
+    // before any operand load is in flight: read inside the tile loop,
+    // their wait would also wait for the next tile's first loads.
+    const GemmParams &pe = p;
+    const Epilogue epi(pe);
 
     // Without CHAIN the body runs once (one tile per workgroup).
     int id = (int)blockIdx.x;
@@ -523,8 +557,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         // 4 columns at a time through the general epilogue with its bounds
         // checks.  With row stride EP_LD = 132 words, the 16 lanes that share an
         // LDS clock touch 16 distinct bank slots.
-        const GemmParams &pe = p;
-        const Epilogue epi(pe);
         // The register path, one row of blocks per iteration at run time,
         // its 4 blocks unrolled (keeps the code and register pressure
         // small); each block's accumulators are picked out through
@@ -534,6 +566,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
             constexpr int OD = decltype(OD_)::value;
             constexpr bool HB = decltype(HB_)::value;
             float macc = 0.0f;   // max |acc| (E4M3 output without bias)
+            uint8_t *const ep_wave = ep_lines + wave * 32 * 128;
 #pragma unroll 1
             for (int i = 0; i < TM; ++i) {
                 nt_unroll<0, TN>([&](auto J) {
@@ -555,11 +588,36 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                     }
                     const uint4 w[4] = {make_uint4(x[0], x[1], x[2], x[3]), make_uint4(x[8], x[9], x[10], x[11]),
                                         make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
-                    const int64_t row = m0 + wm0 + i * 32 + lr;
-                    const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                    vmax = nt_store16<MMA::INT_ACC, OD, HB>(pe, epi, w, row, col, vmax, macc);
+                    if constexpr (OD == DT_E4M3 && !HB) {
+                        // Codes of columns 32j + 16h .. +15 of row lr into
+                        // the wave's staging lines.
+                        const int c = 2 * j + h;
+                        *reinterpret_cast<uint4 *>(ep_wave + lr * 128 + ((c ^ nt_line_swz(lr)) << 4)) =
+                            nt_e4m3_codes16<MMA::INT_ACC>(epi, w, macc);
+                    } else {
+                        const int64_t row = m0 + wm0 + i * 32 + lr;
+                        const int64_t col = n0 + wn0 + j * 32 + h * 16;
+                        vmax = nt_store16<MMA::INT_ACC, OD, HB>(pe, epi, w, row, col, vmax, macc);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                if constexpr (OD == DT_E4M3 && !HB) {
+                    // Whole lines out: store k covers rows 8k .. 8k+7 of the
+                    // row of blocks, eight lanes (128 bytes) per row,
+                    // streamed past the caches (a 128-byte line per eight
+                    // lanes writes whole lines; the codes are not re-read
+                    // by this kernel, and the memory-side cache stays with
+                    // the operands).
+                    const int ch = lane & 7;
+                    nt_unroll<0, 4>([&](auto KK) {
+                        constexpr int k = decltype(KK)::value;
+                        const int r = 8 * k + (lane >> 3);
+                        const uint4 v = *reinterpret_cast<const uint4 *>(ep_wave + r * 128 + ((ch ^ nt_line_swz(r)) << 4));
+                        nt_store16_stream(static_cast<uint8_t *>(pe.out) + (m0 + wm0 + i * 32 + r) * pe.ldo + n0 + wn0 +
+                                              ch * 16,
+                                          v);
+                    });
+                }
             }
             if constexpr (OD == DT_E4M3 && !HB) {
                 const uint32_t b = __float_as_uint(macc * __builtin_fabsf(epi.s_ab));
