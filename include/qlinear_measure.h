@@ -1,7 +1,8 @@
 /* qlinear_measure.h -- a measurement aid of libqlinear.so, outside the
  * method: a streaming kernel with the access pattern of the quantize cast
- * (16-byte loads, 32 bytes read and optionally 16 bytes written per unit,
- * the same grid shape) and none of its arithmetic.  Its rate is the
+ * (16-byte non-temporal loads and plain stores, 32 bytes read and
+ * optionally 16 bytes written per unit, the same grid shape) and none of
+ * its arithmetic.  Its rate is the
  * memory system's ceiling for that pattern, against which the quantize
  * rates are read; the benchmark times it next to them.
  *
