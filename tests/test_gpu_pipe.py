@@ -178,3 +178,48 @@ def test_pipe_128x64_epilogues(orc):
     assert amax8 == amax
     print("128x64 e4m3 differing codes:", check_fp8_out(out8.numpy()[ms, ns], v, S, H, sasb, K, os_, orc,
                                                         bias=bias_of(bias, ns), what="128x64 e4m3"))
+
+
+# More shapes on the pipelined kernel, every output kind of its register
+# epilogue.  (M, N, K, tile): two 128 x 128 tiles per CU (two workgroups per
+# CU); 544 tiles (the grid does not divide into CUs); twelve steps per
+# tile; 272 tiles of 128 x 128 (one workgroup per CU, a second partial
+# wave); 384 tiles of 128 x 64.
+MORE = [(2048, 4096, 1024, (128, 128)), (2176, 4096, 512, (128, 128)), (1024, 8192, 1536, (128, 128)),
+        (2048, 2176, 512, (128, 128)), (2048, 1536, 1024, (128, 64))]
+
+
+@pytest.mark.parametrize("shape", MORE)
+def test_pipe_output_kinds(orc, shape):
+    """BF16 with a bias, FP32 with out_amax (exactly max |out|), E4M3 with
+    out_amax, mixed formats, and INT8 with raw INT32 output (bit-exact),
+    sampled on every tile."""
+    M, N, K, (tm, tn) = shape
+    ms, ns = _entries(M, N, tm, tn, 101)
+    a = finite_codes(orc, 102, 0, M, K, 0)
+    b = finite_codes(orc, 103, 0, N, K, 0)
+    bias = synth.normal(104, 0, N, 0.5)
+    sa, sb = [0.004], [0.75]
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, a, 0, 0, b, 0, 0, K, ms, ns, sa, sb)
+    vb = v + bias.astype(np.float64)[ns]
+    out = run_gpu(a, 0, 0, b, 0, 0, K, sa, 0, sb, 0, bias=bias, out_dtype="bf16")
+    print("pipe bf16", check_float(out_values(out)[ms, ns], vb, S, H, sasb, K, bias=bias_of(bias, ns),
+                                         what=f"pipe {shape} bf16"))
+    out32, amax = run_gpu(a, 0, 0, b, 0, 0, K, sa, 0, sb, 0, out_dtype="fp32", out_amax=True)
+    check_float(out32.numpy()[ms, ns], v, S, H, sasb, K, what=f"pipe {shape} fp32")
+    assert amax == np.abs(out32.numpy()).max()
+    os_ = np.float32(amax / 448.0)
+    out8, amax8 = run_gpu(a, 0, 0, b, 0, 0, K, sa, 0, sb, 0, out_dtype="e4m3", out_scale=os_, out_amax=True)
+    assert amax8 == amax
+    check_fp8_out(out8.numpy()[ms, ns], v, S, H, sasb, K, os_, orc, what=f"pipe {shape} e4m3")
+    # E5M2 x E4M3
+    g = finite_codes(orc, 105, 1, M, K, 1)
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, g, 1, 0, b, 0, 0, K, ms, ns, sa, sb)
+    out = run_gpu(g, 1, 0, b, 0, 0, K, sa, 0, sb, 0, out_dtype="bf16")
+    check_float(out_values(out)[ms, ns], v, S, H, sasb, K, what=f"pipe {shape} e5m2 x e4m3")
+    # INT8, raw INT32
+    ai = finite_codes(orc, 106, 2, M, K, 2)
+    bi = finite_codes(orc, 107, 2, N, K, 2)
+    outi = run_gpu(ai, 2, 0, bi, 2, 0, K, sa, 0, sb, 0, out_dtype="int32")
+    _, _, iacc, _ = orc.qgemm_entries(ai, 2, 0, bi, 2, 0, K, ms, ns)
+    assert np.array_equal(outi.numpy()[ms, ns].astype(np.int64), iacc)
