@@ -268,3 +268,42 @@ def test_linear_forward_static_handworked(orc):
     assert r.amax_x.item() == float(g["amax_x"][0])
     assert r.sx.cpu().numpy()[0] == np.float32(3) / np.float32(57344)
     assert r.out.cpu().numpy().ravel().tolist() == [float(v) for v in g["v"]]
+
+
+def test_linear_forward_large_fp8_as_benchmarked(orc):
+    """The call the benchmark times, at full size: one ql_linear_forward on
+    the large FP8 workload (a [16384, 8192], b [8192, 8192] BF16; per-tensor
+    E4M3; the persistent GEMM with E4M3 output, out_scale = amax_prev/448,
+    out_amax).  Codes and steps of both operands bit-exact; the output codes
+    on 8 full rows, 8 full columns, 4096 random entries and one entry in
+    every 256 x 256 tile inside the E4M3 acceptance set; out_amax equal to
+    max |out| of an FP32-output run of the same product (both are max
+    |fl32(acc * sa * sb)|) and no smaller than the sampled references."""
+    from test_gpu_qgemm import sampled_entries, per_tile_entries, oracle_entries_threaded, run_gpu
+    d = synth.workload("large_fp8")
+    a, b = d["a"], d["b"]
+    aq, sa, ama = orc.quantize(synth.bf16_bits(a), 0, 0)
+    bq, sb, amb = orc.quantize(synth.bf16_bits(b), 0, 0)
+    M, K = aq.shape
+    N = bq.shape[0]
+    ms, ns = sampled_entries(M, N, rows=8, cols=8, rand=4096, seed=16)
+    tms, tns = per_tile_entries(M, N, 256, seed=17)
+    ms, ns = np.concatenate([ms, tms]), np.concatenate([ns, tns])
+    acc, S, _, H, v, sasb = oracle_entries_threaded(orc, aq, 0, 0, bq, 0, 0, K, ms, ns, sa, sb)
+    os_ = np.float32(np.abs(v).max() / 448.0)
+    ag, bg = a.cuda(), b.cuda()
+    r = q.linear_forward(ag, bg, None, "e4m3", out_dtype="e4m3",
+                         out_scale=torch.tensor([os_], dtype=torch.float32, device="cuda"), out_amax=True)
+    torch.cuda.synchronize()
+    del ag, bg
+    assert np.array_equal(r.x_q.cpu().numpy(), aq) and np.array_equal(r.w_q.cpu().numpy(), bq)
+    for got, ref in ((r.sx, sa), (r.amax_x, ama), (r.sw, sb), (r.amax_w, amb)):
+        assert got.cpu().numpy().view(np.uint32)[0] == np.asarray(ref, np.float32).view(np.uint32)[0]
+    codes = r.out.cpu().numpy()[ms, ns]
+    differ = check_fp8_out(codes, v, S, H, sasb, K, os_, orc, what="linear_forward large_fp8")
+    print("linear_forward large_fp8 differing codes:", differ, "of", codes.size)
+    amax = r.out_amax.item()
+    out32, amax32 = run_gpu(aq, 0, 0, bq, 0, 0, K, sa, 0, sb, 0, out_dtype="fp32", out_amax=True)
+    assert amax == amax32 == np.abs(out32.numpy()).max()
+    from tolerance import float_bound
+    assert amax >= (np.abs(v) - float_bound(v, S, H, sasb)).max()
