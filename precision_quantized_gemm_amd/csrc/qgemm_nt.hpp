@@ -594,6 +594,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
                         const int c = 2 * j + h;
                         *reinterpret_cast<uint4 *>(ep_wave + lr * 128 + ((c ^ nt_line_swz(lr)) << 4)) =
                             nt_e4m3_codes16<MMA::INT_ACC>(epi, w, macc);
+                    } else if constexpr (MMA::INT_ACC && OD == DT_INT32) {
+                        // Raw INT32: the block's 32 rows x 128 bytes go
+                        // through the staging lines on their own (lane:
+                        // row lr, chunks 4h .. 4h+3), then out as whole
+                        // lines, streamed like the E4M3 codes.
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<uint4 *>(ep_wave + lr * 128 + (((4 * h + q) ^ nt_line_swz(lr)) << 4)) = w[q];
+                        const int ch = lane & 7;
+                        nt_unroll<0, 4>([&](auto KK) {
+                            constexpr int k = decltype(KK)::value;
+                            const int r = 8 * k + (lane >> 3);
+                            const uint4 v =
+                                *reinterpret_cast<const uint4 *>(ep_wave + r * 128 + ((ch ^ nt_line_swz(r)) << 4));
+                            nt_store16_stream(reinterpret_cast<uint8_t *>(static_cast<int32_t *>(pe.out) +
+                                                                          (m0 + wm0 + i * 32 + r) * pe.ldo + n0 + wn0 +
+                                                                          j * 32 + ch * 4),
+                                              v);
+                        });
                     } else {
                         const int64_t row = m0 + wm0 + i * 32 + lr;
                         const int64_t col = n0 + wn0 + j * 32 + h * 16;
