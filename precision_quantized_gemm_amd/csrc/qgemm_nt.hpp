@@ -207,10 +207,15 @@ __device__ __forceinline__ void nt_store16_stream(uint8_t *dst, uint4 c)
 // Returns the running max |v| as FP32 bits.
 // OD: the output dtype, fixed at compile time by the caller's dispatch;
 // HB: whether a bias is present (its kind is still tested at run time).
-template <bool INT_ACC, int OD, bool HB>
+// STAGE (BF16 output): the two 16-byte halves go to the LDS addresses
+// stage0 / stage1 instead of the output, for a caller that writes whole
+// lines.
+template <bool INT_ACC, int OD, bool HB, bool STAGE = false>
 __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilogue &epi, const uint4 (&w)[4],
-                                               int64_t row, int64_t col, uint32_t vmax, float &macc)
+                                               int64_t row, int64_t col, uint32_t vmax, float &macc,
+                                               uint8_t *stage0 = nullptr, uint8_t *stage1 = nullptr)
 {
+    static_assert(!STAGE || OD == DT_BF16, "staged halves are BF16 rows");
     if constexpr (OD == DT_E4M3 && !HB) {
         *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.out) + row * p.ldo + col) =
             nt_e4m3_codes16<INT_ACC>(epi, w, macc);
@@ -288,9 +293,14 @@ __device__ __forceinline__ uint32_t nt_store16(const GemmParams &p, const Epilog
         for (int e = 0; e < 8; ++e)
             hw[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * e]) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * e + 1]) << 16);
-        uint4 *out = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + o);
-        out[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        out[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        if constexpr (STAGE) {
+            *reinterpret_cast<uint4 *>(stage0) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4 *>(stage1) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        } else {
+            uint4 *out = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + o);
+            out[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            out[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        }
     } else {
         float4 *out = reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o);
 #pragma unroll

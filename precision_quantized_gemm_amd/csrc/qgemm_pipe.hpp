@@ -358,6 +358,11 @@ __global__ __launch_bounds__(GEMM_THREADS, OCC) __attribute__((amdgpu_waves_per_
     auto regs_rows = [&](auto OD_, auto HB_) {
         constexpr int OD = decltype(OD_)::value;
         constexpr bool HB = decltype(HB_)::value;
+        // BF16 rows of a 64-column wave tile are 128 bytes: each row of
+        // blocks goes through 4 KiB of LDS per wave (the stages are free
+        // now) and out as whole lines.
+        constexpr bool LINES = OD == DT_BF16 && WN == 64;
+        uint8_t *const ep_wave = lds + wave * 32 * 128;
         float macc = 0.0f;
 #pragma unroll 1
         for (int i = 0; i < TM; ++i) {
@@ -382,9 +387,33 @@ __global__ __launch_bounds__(GEMM_THREADS, OCC) __attribute__((amdgpu_waves_per_
                                     make_uint4(x[4], x[5], x[6], x[7]), make_uint4(x[12], x[13], x[14], x[15])};
                 const int64_t row = m0 + wm0 + i * 32 + lr;
                 const int64_t col = n0 + wn0 + j * 32 + h * 16;
-                vmax = nt_store16<MMA::INT_ACC, OD, HB>(p, epi, w, row, col, vmax, macc);
+                if constexpr (LINES) {
+                    // BF16 columns 32j + 16h .. +15 of row lr: chunks
+                    // 4j + 2h and 4j + 2h + 1 of the row's 128 bytes.
+                    const int c = 4 * j + 2 * h;
+                    vmax = nt_store16<MMA::INT_ACC, OD, HB, true>(
+                        p, epi, w, row, col, vmax, macc, ep_wave + lr * 128 + ((c ^ nt_line_swz(lr)) << 4),
+                        ep_wave + lr * 128 + (((c + 1) ^ nt_line_swz(lr)) << 4));
+                } else {
+                    vmax = nt_store16<MMA::INT_ACC, OD, HB>(p, epi, w, row, col, vmax, macc);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (LINES) {
+                // Whole 128-byte lines out, streamed past the caches: store
+                // k covers rows 8k .. 8k+7 of the row of blocks, eight lanes
+                // per row (MLP-up forward 15.7 -> 15.1 us, dW 12.9 -> 12.6
+                // us; plain stores of the same lines: 15.3 and 13.0 us).
+                const int ch = lane & 7;
+                nt_unroll<0, 4>([&](auto KK) {
+                    constexpr int k = decltype(KK)::value;
+                    const int r = 8 * k + (lane >> 3);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ep_wave + r * 128 + ((ch ^ nt_line_swz(r)) << 4));
+                    nt_store16_stream(reinterpret_cast<uint8_t *>(static_cast<uint16_t *>(p.out) +
+                                                                  (m0 + wm0 + i * 32 + r) * p.ldo + n0 + wn0 + ch * 8),
+                                      v);
+                });
+            }
         }
         if constexpr (OD == DT_E4M3 && !HB) {
             const uint32_t b = __float_as_uint(macc * __builtin_fabsf(epi.s_ab));
