@@ -91,6 +91,15 @@ template <int AF, int BF> struct Mma32 {
         const v8i b = __builtin_shufflevector((v4i)b0, (v4i)b1, 0, 1, 2, 3, 4, 5, 6, 7);
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
     }
+    // The same with a zero accumulator in (the first k of a tile): the
+    // instruction's inline constant, so no register needs clearing.
+    __device__ __forceinline__ static void run0(acc_t &c, const u32x4 &a0, const u32x4 &a1, const u32x4 &b0,
+                                                const u32x4 &b1)
+    {
+        const v8i a = __builtin_shufflevector((v4i)a0, (v4i)a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i b = __builtin_shufflevector((v4i)b0, (v4i)b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc_t{}, AF, BF, 0, 0, 0, 0);
+    }
     __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return __float_as_uint(c[r]); }
 };
 
@@ -106,6 +115,12 @@ template <> struct Mma32<FMT_INT8, FMT_INT8> {
                                                const u32x4 &b1)
     {
         c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a0, (v4i)b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a1, (v4i)b1, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static void run0(acc_t &c, const u32x4 &a0, const u32x4 &a1, const u32x4 &b0,
+                                                const u32x4 &b1)
+    {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a0, (v4i)b0, acc_t{}, 0, 0, 0);
         c = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i)a1, (v4i)b1, c, 0, 0, 0);
     }
     __device__ __forceinline__ static uint32_t bits(const acc_t &c, int r) { return (uint32_t)c[r]; }
@@ -422,6 +437,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         const int i = t >> 2, j = t & 3;
         MMA::run(acc[i][j], f[2 * (TM + j)], f[2 * (TM + j) + 1], f[2 * i], f[2 * i + 1]);
     };
+    auto mma0 = [&](u32x4 (&f)[16], int t) {
+        const int i = t >> 2, j = t & 3;
+        MMA::run0(acc[i][j], f[2 * (TM + j)], f[2 * (TM + j) + 1], f[2 * i], f[2 * i + 1]);
+    };
 
     // CHAIN (the launcher guarantees: every tile whole, the register
     // epilogue, an even number of whole k-steps): the next tile's first two
@@ -449,10 +468,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         const int next = id + (int)gridDim.x;
         const bool chain = CHAIN && next < total;
 
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
 
         // One k-step worked from stage S (= kt % 2).  Half 0: MFMAs on set 0
         // while half 1's fragments are read into set 1 (front-loaded,
@@ -463,7 +478,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         // wave).  At the mid-step barrier everyone's loads of step kt+1 have
         // landed.  Half 1: MFMAs on set 1 while step kt+1's half-0 fragments
         // are read from the other stage into set 0, and the refill goes on.
-        auto step = [&](auto S, int kt) {
+        auto step = [&](auto S, auto FIRST, int kt) {
             constexpr int STAGE = decltype(S)::value;
             typedef std::integral_constant<int, 1 - STAGE> SN;
             const bool to_next = chain && kt + 2 >= nk;
@@ -489,7 +504,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
             };
             nt_unroll<0, 16>([&](auto T) {
                 constexpr int t = decltype(T)::value;
-                mma(f0, t);
+                if constexpr (decltype(FIRST)::value) mma0(f0, t);
+                else mma(f0, t);
                 nt_unroll<0, RPS>([&](auto R) {
                     constexpr int r = t * RPS + decltype(R)::value;
                     if constexpr (r < 16) f1[r] = read_frag(S, I1{}, std::integral_constant<int, r>{});
@@ -541,10 +557,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void qgemm_nt_kernel(GemmParams p)
         }
         // Steps past the end read stale fragments that no MFMA uses (or,
         // chaining, the next tile's first ones); the loop runs two steps per
-        // iteration so each step's stage is a constant.
-        for (int kt = 0; kt < nk; kt += 2) {
-            step(I0{}, kt);
-            if (kt + 1 < nk) step(I1{}, kt + 1);
+        // iteration so each step's stage is a constant.  The first step's
+        // first half starts every block from a zero accumulator (clearing
+        // the 256 accumulator registers between two chained tiles cost
+        // about 1%).
+        step(I0{}, std::true_type{}, 0);
+        if (1 < nk) step(I1{}, std::false_type{}, 1);
+        for (int kt = 2; kt < nk; kt += 2) {
+            step(I0{}, std::false_type{}, kt);
+            if (kt + 1 < nk) step(I1{}, std::false_type{}, kt + 1);
         }
         if (!chain) {
             __builtin_amdgcn_s_waitcnt(0x0F70);
