@@ -205,10 +205,19 @@ __device__ __forceinline__ uint4 nt_e4m3_codes16(const Epilogue &epi, const uint
 }
 
 // Position of 16-byte chunk c of row r in a wave's 32-row x 128-byte line
-// staging area (E4M3 epilogue): c ^ g(r).  Writes (lane l: row l % 32,
-// chunk 2j + l / 32) and reads (lane l: row 8k + l / 8, chunk l % 8) then
-// put the lanes that share an LDS clock on distinct 16-byte bank slots.
-__device__ __forceinline__ int nt_line_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 3) & 3); }
+// staging area (the whole-line epilogues): c ^ g(r), with g's bits r1,
+// r3 and r2 ^ r4.  Writes (lane l: row l % 32, one chunk per half-wave) and
+// reads (lane l: row 8k + l / 8, chunk l % 8) then put the 16 lanes of one
+// LDS clock on 16 distinct 16-byte bank slots whether a clock takes lanes
+// 16i .. 16i+15 or the alternate lane quads of a half-wave (the 16-byte
+// reads' grouping): two rows of equal parity in either group differ in
+// g, and rows 8k and 8k+2 (8k+1 and 8k+3) differ in its bit 2.  Without
+// the r2 term the writes conflicted two-way (the bank-conflict counter
+// read 3.7 M cycles per large GEMM).
+__device__ __forceinline__ int nt_line_swz(int r)
+{
+    return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | (((r >> 2) ^ (r >> 4)) & 1);
+}
 
 __device__ __forceinline__ void nt_store16_stream(uint8_t *dst, uint4 c)
 {
