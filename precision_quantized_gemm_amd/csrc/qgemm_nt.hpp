@@ -205,19 +205,16 @@ __device__ __forceinline__ uint4 nt_e4m3_codes16(const Epilogue &epi, const uint
 }
 
 // Position of 16-byte chunk c of row r in a wave's 32-row x 128-byte line
-// staging area (the whole-line epilogues): c ^ g(r), with g's bits r1,
-// r3 and r2 ^ r4.  Writes (lane l: row l % 32, one chunk per half-wave) and
-// reads (lane l: row 8k + l / 8, chunk l % 8) then put the 16 lanes of one
-// LDS clock on 16 distinct 16-byte bank slots whether a clock takes lanes
-// 16i .. 16i+15 or the alternate lane quads of a half-wave (the 16-byte
-// reads' grouping): two rows of equal parity in either group differ in
-// g, and rows 8k and 8k+2 (8k+1 and 8k+3) differ in its bit 2.  Without
-// the r2 term the writes conflicted two-way (the bank-conflict counter
-// read 3.7 M cycles per large GEMM).
-__device__ __forceinline__ int nt_line_swz(int r)
-{
-    return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | (((r >> 2) ^ (r >> 4)) & 1);
-}
+// staging area (the whole-line epilogues): c ^ f(r), the operand stages'
+// swizzle.  Writes (lane l: row l % 32, one chunk per half-wave) and reads
+// (lane l: row 8k + l / 8, chunk l % 8) then put the 16 lanes of one LDS
+// clock on 16 distinct 16-byte bank slots, both when a clock takes the
+// lane quads of a half-wave whose quad index has equal parity (how the
+// 16-byte reads are served) and when it takes lanes 16i .. 16i+15 (the
+// 16-byte writes behave like the latter).  An earlier swizzle here,
+// 4 r1 + (r >> 3 & 3), conflicted two-way on the reads and on the writes
+// (the bank-conflict counter read 3.7 M cycles per large GEMM).
+__device__ __forceinline__ int nt_line_swz(int r) { return nt_swz(r); }
 
 __device__ __forceinline__ void nt_store16_stream(uint8_t *dst, uint4 c)
 {
