@@ -505,6 +505,83 @@ def test_pipelined_chained_grid(orc, K, out_dtype, bias_kind, af, bf):
                                           what=f"chained {out_dtype}"))
 
 
+def test_chained_grid_int32_every_entry(orc):
+    """The persistent grid with raw INT32 output, every entry of the output:
+    272 whole 256 x 256 tiles on one workgroup per CU (so some workgroups
+    walk two tiles and chain into the second), the output leaving through
+    the per-wave line staging.  The reference is the product of the decoded
+    INT8 codes as a float64 matrix product, exact here (|acc| <= 127^2 * 256
+    < 2^53), so every INT32 must match it bit for bit."""
+    M, N, K = 16 * 256, 17 * 256, 256
+    a = finite_codes(orc, 91, 2, M, K, 2)
+    b = finite_codes(orc, 92, 2, N, K, 2)
+    out = run_gpu(a, 2, 0, b, 2, 0, K, [1.0], 0, [1.0], 0, out_dtype="int32")
+    ref = a.view(np.int8).astype(np.float64) @ b.view(np.int8).astype(np.float64).T
+    got = out.numpy()
+    assert got.dtype == np.int32 and got.shape == (M, N)
+    bad = np.argwhere(got.astype(np.float64) != ref)
+    assert bad.size == 0, f"{len(bad)} entries differ, first {bad[:4].tolist()}"
+    # the oracle agrees on a sample (it is the reference of every other test)
+    ms, ns = sampled_entries(M, N, rows=1, cols=1, rand=256, seed=93)
+    _, _, iacc, _ = orc.qgemm_entries(a, 2, 0, b, 2, 0, K, ms, ns)
+    assert np.array_equal(got[ms, ns].astype(np.int64), iacc)
+
+
+def test_chained_grid_e4m3_every_entry(orc):
+    """The persistent grid's E4M3 output (codes staged per wave into whole
+    128-byte lines) and its out_amax, every entry.  INT8 codes with
+    per-tensor scales and no bias make each code exactly predictable: the
+    epilogue multiplies the exact integer accumulator, as FP32, by
+    fl32(fl32(sa * sb) * fl32(1 / out_scale)) and encodes the FP32 result
+    with round to nearest even and saturation (the oracle's encoder does
+    that step), and out_amax is fl32(max |acc| * fl32(sa * sb)).  The step
+    is chosen so that the largest values saturate."""
+    M, N, K = 16 * 256, 17 * 256, 256
+    a = finite_codes(orc, 97, 2, M, K, 2)
+    b = finite_codes(orc, 98, 2, N, K, 2)
+    sa, sb = np.float32(0.0117), np.float32(0.0031)
+    acc = a.view(np.int8).astype(np.float64) @ b.view(np.int8).astype(np.float64).T
+    s_ab = np.float32(sa * sb)
+    amax_ref = np.float32(np.float32(np.abs(acc).max()) * s_ab)
+    out_scale = np.float32(amax_ref / np.float32(448.0) * np.float32(0.75))
+    out, amax = run_gpu(a, 2, 0, b, 2, 0, K, [sa], 0, [sb], 0, out_dtype="e4m3", out_scale=out_scale, out_amax=True)
+    assert np.float32(amax) == amax_ref
+    s_out = np.float32(s_ab * np.float32(np.float32(1.0) / out_scale))
+    u = acc.astype(np.float32) * s_out
+    ref = orc.fp8_output(u.astype(np.float64).ravel(), 1.0).reshape(M, N)
+    got = out.numpy()
+    assert got.shape == (M, N)
+    assert (ref == 0x7E).any() and (ref == 0xFE).any(), "the step makes the largest values saturate"
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K,lay", [(2048, 4096, 1024, 0), (2048, 2048, 512, 0), (4096, 1024, 2048, 1)])
+def test_pipelined_bf16_lines_every_entry(orc, M, N, K, lay):
+    """The pipelined kernel's whole-line BF16 output (128 x 128 tiles: two
+    workgroups per CU for 2048 x 4096, one for 2048 x 2048, both operands
+    MN-major for 4096 x 1024), every entry.  INT8 codes with per-tensor
+    scales make every entry exactly predictable: the accumulator is the
+    exact integer product (a float64 matrix product of the decoded codes,
+    exact here), the epilogue multiplies its FP32 value by the FP32 product
+    of the scales and rounds to BF16 to nearest even.  The GPU output must
+    match that bit for bit; the oracle agrees on a sample."""
+    a = finite_codes(orc, 94, 2, M, K, 2)
+    b = finite_codes(orc, 95, 2, N, K, 2)
+    sa, sb = np.float32(0.0123), np.float32(0.00457)
+    out = run_gpu(storage(a, lay), 2, lay, storage(b, lay), 2, lay, K, [sa], 0, [sb], 0, out_dtype="bf16")
+    acc = a.view(np.int8).astype(np.float64) @ b.view(np.int8).astype(np.float64).T
+    assert np.abs(acc).max() < 2 ** 24
+    v32 = acc.astype(np.float32) * np.float32(sa * sb)
+    ref = torch.from_numpy(v32).to(torch.bfloat16)
+    assert out.dtype == torch.bfloat16 and out.shape == (M, N)
+    bad = torch.nonzero(out.view(torch.int16) != ref.view(torch.int16))
+    assert bad.numel() == 0, f"{bad.shape[0]} entries differ, first {bad[:4].tolist()}"
+    ms, ns = sampled_entries(M, N, rows=1, cols=1, rand=256, seed=96)
+    _, _, iacc, _ = orc.qgemm_entries(storage(a, lay), 2, lay, storage(b, lay), 2, lay, K, ms, ns)
+    assert np.array_equal(acc[ms, ns].astype(np.int64), iacc)
+
+
 @pytest.mark.parametrize("M,N,K,out_dtype,sag", [(8192, 5120, 512, "int32", 1), (8192, 5120, 256, "bf16", 0),
                                                  (4096 + 37, 4096 + 48, 1024, "fp32", 1),
                                                  (4096, 4096, 1040, "int32", 0)])
